@@ -1,0 +1,160 @@
+/*
+ * paged_attention.h -- C ABI of libpagedattn.so, an MI355X (gfx950) paged
+ * attention operator.
+ *
+ * The operation ("Week 3 Day 5: Paged FlashAttention", sections "Keep the
+ * Day 4 Interface", Task 1 and Task 2; "Week 2 Day 5: Fused Decode
+ * Attention", Task 1): for every sequence b, query head h and query row l,
+ *
+ *   out[b,h,l,:] = sum_s softmax_s( scale * q[b,h,l,:] . K_b[s,:] ) * V_b[s,:]
+ *
+ * over the visible logical key positions s of sequence b, where
+ *   - logical position s lives in physical page block_table[b, s / page_size]
+ *     at slot s % page_size, i.e. K_b[s,:] = key_pages[page, kv_head, slot, :]
+ *     (Task 1 of "Week 3 Day 5");
+ *   - kv_head = h / (num_q_heads / num_kv_heads) (GQA head map, Task 1 of
+ *     "Week 2 Day 5");
+ *   - with causal != 0, key s is visible to row l iff
+ *     s <= l + context_lens[b] - query_len (Task 2 of "Week 3 Day 5"), so the
+ *     query_len rows are the last query_len positions of the context; with
+ *     causal == 0 every s < context_lens[b] is visible.
+ * The result is exact attention; only the order of loads and reductions
+ * differs from a dense softmax. Arithmetic: bf16 loads, fp32 dot products,
+ * softmax state and accumulation, bf16 (round to nearest even) output.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays.
+ *     bf16 is stored as 16-bit words. All index arrays are int32.
+ *   - The caller owns every buffer. The library allocates nothing, keeps no
+ *     pointer after returning, and has no global state besides the
+ *     thread-local error message. `out` must not alias any input.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously; results are valid after the stream
+ *     is synchronised.
+ *   - Return value: PA_OK, or a negative PA_ERR_* code. Every argument check
+ *     happens before any launch; on an error nothing is enqueued, nothing
+ *     aborts, and paged_attention_last_error() describes the problem.
+ */
+#ifndef PAGED_ATTENTION_H_
+#define PAGED_ATTENTION_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,     /* null pointer, non-positive size, H_q % H_kv != 0,
+                              max_pages * page_size < query_len, ... */
+  PA_ERR_UNSUPPORTED = -2, /* head_dim != 128, or a size past a kernel limit */
+  PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  PA_ERR_LAUNCH = -4,      /* the HIP runtime rejected a launch */
+  PA_ERR_METADATA = -5     /* paged_attention_check_metadata found bad data */
+};
+
+/* Which schedule runs. AUTO picks by query length (see paged_attention). */
+enum {
+  PA_SCHEDULE_AUTO = 0,
+  PA_SCHEDULE_DECODE = 1,  /* short-query split-context schedule */
+  PA_SCHEDULE_PREFILL = 2  /* long-query MFMA tiled schedule */
+};
+
+/*
+ * paged_attention -- the operator (one call, "Week 3 Day 5", section "Keep
+ * the Day 4 Interface"; the mask="causal" argument there is `causal`).
+ *
+ *   query        bf16 [batch, num_q_heads, query_len, head_dim]
+ *   key_pages    bf16 [num_pages, num_kv_heads, page_size, head_dim]
+ *   value_pages  bf16 [num_pages, num_kv_heads, page_size, head_dim]
+ *   block_table  int32 [batch, max_pages]; entry j of row b is the physical
+ *                page holding logical positions [j*page_size, (j+1)*page_size)
+ *   context_lens int32 [batch]; number of logical K/V positions of sequence b
+ *   out          bf16 [batch, num_q_heads, query_len, head_dim], written once
+ *   scale        multiplier of q.k (typically 1/sqrt(head_dim))
+ *   causal       0 or 1
+ *   workspace    device scratch of at least
+ *                paged_attention_workspace_bytes(...) bytes (may be NULL when
+ *                that is 0); its contents need no initialisation and are
+ *                garbage afterwards. Calls that share a workspace must be
+ *                ordered on one stream.
+ *
+ * Device-data preconditions (not checked; see
+ * paged_attention_check_metadata): for every b,
+ * 1 <= context_lens[b] <= max_pages * page_size; with causal,
+ * context_lens[b] >= query_len; 0 <= block_table[b,j] < num_pages for
+ * j < ceil(context_lens[b] / page_size). Table entries past that and page
+ * slots at or past context_lens[b] are never read and may hold anything.
+ *
+ * Dispatch (inside the library, "Week 3 Day 5", Task 4): a short query
+ * (query_len * num_q_heads / num_kv_heads <= 8) runs the decode schedule,
+ * anything longer the prefill schedule. Supported: head_dim == 128,
+ * page_size >= 1, any batch, GQA ratio and context length that fit int32.
+ */
+int paged_attention(const void* query, const void* key_pages, const void* value_pages,
+                    const int32_t* block_table, const int32_t* context_lens, void* out,
+                    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t query_len,
+                    int32_t head_dim, int32_t num_pages, int32_t page_size, int32_t max_pages,
+                    float scale, int32_t causal, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * paged_attention_ex -- paged_attention with the schedule and the decode
+ * split length chosen by the caller (for tests of both schedules on one
+ * input, "Week 3 Day 5", Task 3, and for tuning sweeps).
+ *   schedule      PA_SCHEDULE_AUTO / _DECODE / _PREFILL. DECODE needs
+ *                 query_len * num_q_heads / num_kv_heads <= 8.
+ *   decode_split  keys per decode work item; 0 = automatic; otherwise a
+ *                 multiple of 256 in [256, 65536] with
+ *                 decode_split / page_size <= 2048.
+ * Same arguments, preconditions and errors as paged_attention otherwise.
+ */
+int paged_attention_ex(const void* query, const void* key_pages, const void* value_pages,
+                       const int32_t* block_table, const int32_t* context_lens, void* out,
+                       int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t query_len,
+                       int32_t head_dim, int32_t num_pages, int32_t page_size, int32_t max_pages,
+                       float scale, int32_t causal, void* workspace, size_t workspace_bytes,
+                       int32_t schedule, int32_t decode_split, void* stream);
+
+/*
+ * Workspace bytes paged_attention (or paged_attention_ex with the same
+ * schedule and decode_split) needs for these sizes; 0 when none is needed.
+ * Returns (size_t)-1 if the sizes are invalid (see
+ * paged_attention_last_error). Pure host arithmetic, no device access.
+ */
+size_t paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t query_len, int32_t head_dim, int32_t page_size,
+                                       int32_t max_pages);
+size_t paged_attention_workspace_bytes_ex(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t query_len, int32_t head_dim, int32_t page_size,
+                                          int32_t max_pages, int32_t schedule, int32_t decode_split);
+
+/*
+ * The schedule PA_SCHEDULE_AUTO resolves to for these sizes (DECODE or
+ * PREFILL), or a negative PA_ERR_* code. Pure host logic.
+ */
+int paged_attention_schedule(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t query_len, int32_t head_dim, int32_t page_size,
+                             int32_t max_pages);
+
+/*
+ * paged_attention_check_metadata -- opt-in debug check of the device-data
+ * preconditions above. Copies block_table and context_lens to the host on
+ * `stream`, synchronises that stream, and returns PA_OK or PA_ERR_METADATA
+ * (with the first offending entry in paged_attention_last_error()).
+ */
+int paged_attention_check_metadata(const int32_t* block_table, const int32_t* context_lens,
+                                   int32_t batch, int32_t max_pages, int32_t num_pages,
+                                   int32_t page_size, int32_t query_len, int32_t causal,
+                                   void* stream);
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char* paged_attention_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTENTION_H_ */

@@ -1,1 +1,24 @@
-"""MI355X-native paged attention (placeholder until the binding lands)."""
+"""MI355X-native paged attention operator.
+
+One operator, ``paged_attention``: exact scaled-dot-product attention over a
+paged K/V pool (logical position -> block_table -> page slot), folded tile by
+tile into an online softmax by hand-written gfx950 HIP kernels behind the C
+ABI of ``include/paged_attention.h`` (``libpagedattn.so``). PyTorch only
+provides device memory and streams.
+
+- ``native``    -- the ctypes binding (``paged_attention``, ``workspace_bytes``,
+  ``schedule_for``, ``check_metadata``)
+- ``workloads`` -- seeded synthetic inputs of the five measured configurations
+- ``build``     -- hipcc build of the shared library
+"""
+
+from .native import (  # noqa: F401
+    SCHEDULE_AUTO,
+    SCHEDULE_DECODE,
+    SCHEDULE_PREFILL,
+    PagedAttentionError,
+    check_metadata,
+    paged_attention,
+    schedule_for,
+    workspace_bytes,
+)

@@ -1,0 +1,31 @@
+// pa_kernels.h -- launch entry points of the two gfx950 schedules, called by
+// the C-ABI layer after validation and planning.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_plan.h"
+
+namespace pa {
+
+struct KernelArgs {
+  const void* query;
+  const void* key_pages;
+  const void* value_pages;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  void* out;
+  void* workspace;
+  int batch, num_q_heads, num_kv_heads, query_len, num_pages, page_size, max_pages;
+  float scale;
+  int causal;
+};
+
+// Short-query split-context schedule (pa_decode.hip).
+hipError_t launch_decode(const KernelArgs& k, const Plan& p, hipStream_t stream);
+
+// Long-query bf16-MFMA tiled schedule (pa_prefill.hip).
+hipError_t launch_prefill(const KernelArgs& k, const Plan& p, hipStream_t stream);
+
+}  // namespace pa

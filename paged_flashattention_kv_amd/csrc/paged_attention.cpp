@@ -1,0 +1,186 @@
+// paged_attention.cpp -- the C ABI declared in include/paged_attention.h:
+// argument checks, planning (pa_plan.cpp) and dispatch to the decode or
+// prefill schedule. Nothing is launched unless every check passes.
+#include "paged_attention.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "pa_kernels.h"
+#include "pa_plan.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_error(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+pa::Shape make_shape(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t query_len,
+                     int32_t head_dim, int32_t num_pages, int32_t page_size, int32_t max_pages,
+                     bool causal) {
+  pa::Shape s;
+  s.batch = batch;
+  s.num_q_heads = num_q_heads;
+  s.num_kv_heads = num_kv_heads;
+  s.query_len = query_len;
+  s.head_dim = head_dim;
+  s.num_pages = num_pages;
+  s.page_size = page_size;
+  s.max_pages = max_pages;
+  s.causal = causal;
+  return s;
+}
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_ex(const void* query, const void* key_pages, const void* value_pages,
+                       const int32_t* block_table, const int32_t* context_lens, void* out,
+                       int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t query_len,
+                       int32_t head_dim, int32_t num_pages, int32_t page_size, int32_t max_pages,
+                       float scale, int32_t causal, void* workspace, size_t workspace_bytes,
+                       int32_t schedule, int32_t decode_split, void* stream) {
+  if (!query || !key_pages || !value_pages || !block_table || !context_lens || !out)
+    return set_error(PA_ERR_INVALID, "a tensor pointer is NULL");
+  if (causal != 0 && causal != 1) return set_error(PA_ERR_INVALID, "causal must be 0 or 1");
+  if (!std::isfinite(scale)) return set_error(PA_ERR_INVALID, "scale must be finite");
+  pa::Plan plan;
+  std::string err;
+  const pa::Shape s = make_shape(batch, num_q_heads, num_kv_heads, query_len, head_dim, num_pages,
+                                 page_size, max_pages, causal != 0);
+  const int rc = pa::make_plan(s, schedule, decode_split, true, &plan, &err);
+  if (rc != pa::kOk) return set_error(rc, err);
+  if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+    return set_error(PA_ERR_WORKSPACE, "workspace smaller than paged_attention_workspace_bytes() = " +
+                                           std::to_string(plan.workspace_bytes));
+  const size_t q_bytes = size_t(batch) * num_q_heads * query_len * head_dim * 2;
+  const size_t pool_bytes = size_t(num_pages) * num_kv_heads * page_size * head_dim * 2;
+  if (overlaps(out, q_bytes, query, q_bytes) || overlaps(out, q_bytes, key_pages, pool_bytes) ||
+      overlaps(out, q_bytes, value_pages, pool_bytes) ||
+      overlaps(out, q_bytes, block_table, size_t(batch) * max_pages * 4) ||
+      overlaps(out, q_bytes, context_lens, size_t(batch) * 4) ||
+      (plan.workspace_bytes > 0 && overlaps(out, q_bytes, workspace, plan.workspace_bytes)))
+    return set_error(PA_ERR_INVALID, "out overlaps an input or the workspace");
+
+  pa::KernelArgs k;
+  k.query = query;
+  k.key_pages = key_pages;
+  k.value_pages = value_pages;
+  k.block_table = block_table;
+  k.context_lens = context_lens;
+  k.out = out;
+  k.workspace = workspace;
+  k.batch = batch;
+  k.num_q_heads = num_q_heads;
+  k.num_kv_heads = num_kv_heads;
+  k.query_len = query_len;
+  k.num_pages = num_pages;
+  k.page_size = page_size;
+  k.max_pages = max_pages;
+  k.scale = scale;
+  k.causal = causal;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = plan.schedule == pa::kScheduleDecode ? pa::launch_decode(k, plan, st)
+                                                            : pa::launch_prefill(k, plan, st);
+  if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, std::string("launch failed: ") + hipGetErrorString(e));
+  g_last_error.clear();
+  return PA_OK;
+}
+
+int paged_attention(const void* query, const void* key_pages, const void* value_pages,
+                    const int32_t* block_table, const int32_t* context_lens, void* out,
+                    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t query_len,
+                    int32_t head_dim, int32_t num_pages, int32_t page_size, int32_t max_pages,
+                    float scale, int32_t causal, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return paged_attention_ex(query, key_pages, value_pages, block_table, context_lens, out, batch,
+                            num_q_heads, num_kv_heads, query_len, head_dim, num_pages, page_size,
+                            max_pages, scale, causal, workspace, workspace_bytes, PA_SCHEDULE_AUTO, 0,
+                            stream);
+}
+
+size_t paged_attention_workspace_bytes_ex(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t query_len, int32_t head_dim, int32_t page_size,
+                                          int32_t max_pages, int32_t schedule, int32_t decode_split) {
+  pa::Plan plan;
+  std::string err;
+  const pa::Shape s = make_shape(batch, num_q_heads, num_kv_heads, query_len, head_dim, 1, page_size,
+                                 max_pages, false);
+  const int rc = pa::make_plan(s, schedule, decode_split, false, &plan, &err);
+  if (rc != pa::kOk) {
+    set_error(rc, err);
+    return static_cast<size_t>(-1);
+  }
+  g_last_error.clear();
+  return plan.workspace_bytes;
+}
+
+size_t paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t query_len, int32_t head_dim, int32_t page_size,
+                                       int32_t max_pages) {
+  return paged_attention_workspace_bytes_ex(batch, num_q_heads, num_kv_heads, query_len, head_dim,
+                                            page_size, max_pages, PA_SCHEDULE_AUTO, 0);
+}
+
+int paged_attention_schedule(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t query_len, int32_t head_dim, int32_t page_size,
+                             int32_t max_pages) {
+  pa::Plan plan;
+  std::string err;
+  const pa::Shape s = make_shape(batch, num_q_heads, num_kv_heads, query_len, head_dim, 1, page_size,
+                                 max_pages, false);
+  const int rc = pa::make_plan(s, PA_SCHEDULE_AUTO, 0, false, &plan, &err);
+  if (rc != pa::kOk) return set_error(rc, err);
+  g_last_error.clear();
+  return plan.schedule;
+}
+
+int paged_attention_check_metadata(const int32_t* block_table, const int32_t* context_lens,
+                                   int32_t batch, int32_t max_pages, int32_t num_pages,
+                                   int32_t page_size, int32_t query_len, int32_t causal,
+                                   void* stream) {
+  if (!block_table || !context_lens) return set_error(PA_ERR_INVALID, "a tensor pointer is NULL");
+  if (batch < 1 || max_pages < 1 || num_pages < 1 || page_size < 1 || query_len < 1)
+    return set_error(PA_ERR_INVALID, "all sizes must be positive");
+  std::vector<int32_t> bt(size_t(batch) * max_pages), ctx(batch);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(bt.data(), block_table, bt.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(ctx.data(), context_lens, ctx.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, std::string("copy failed: ") + hipGetErrorString(e));
+  const int64_t max_ctx = int64_t(max_pages) * page_size;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t c = ctx[b];
+    if (c < 1 || c > max_ctx)
+      return set_error(PA_ERR_METADATA, "context_lens[" + std::to_string(b) + "] = " + std::to_string(c) +
+                                            " outside [1, max_pages * page_size]");
+    if (causal && c < query_len)
+      return set_error(PA_ERR_METADATA, "context_lens[" + std::to_string(b) + "] < query_len under causal");
+    const int64_t used = (int64_t(c) + page_size - 1) / page_size;
+    for (int64_t j = 0; j < used; ++j) {
+      const int32_t p = bt[size_t(b) * max_pages + j];
+      if (p < 0 || p >= num_pages)
+        return set_error(PA_ERR_METADATA, "block_table[" + std::to_string(b) + "][" + std::to_string(j) +
+                                              "] = " + std::to_string(p) + " is not a page of the pool");
+    }
+  }
+  g_last_error.clear();
+  return PA_OK;
+}
+
+const char* paged_attention_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,204 @@
+"""ctypes binding of libpagedattn.so (the C ABI of include/paged_attention.h).
+
+Argument marshalling only: every step of the operator runs in the library's
+HIP kernels. PyTorch supplies device memory and the current stream. If the
+library has not been built this module raises at first use -- there is no
+fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+
+PA_OK = 0
+PA_ERR_INVALID = -1
+PA_ERR_UNSUPPORTED = -2
+PA_ERR_WORKSPACE = -3
+PA_ERR_LAUNCH = -4
+PA_ERR_METADATA = -5
+
+SCHEDULE_AUTO = 0
+SCHEDULE_DECODE = 1
+SCHEDULE_PREFILL = 2
+
+# Every symbol include/paged_attention.h declares.
+EXPORTED = (
+    "paged_attention",
+    "paged_attention_ex",
+    "paged_attention_workspace_bytes",
+    "paged_attention_workspace_bytes_ex",
+    "paged_attention_schedule",
+    "paged_attention_check_metadata",
+    "paged_attention_last_error",
+)
+
+_lib = None
+_lock = threading.Lock()
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"paged_attention error {code}: {message}")
+        self.code = code
+
+
+def load() -> ctypes.CDLL:
+    """Load the shared library (once) and declare argument types."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m paged_flashattention_kv_amd.build` "
+                "(the operator has no non-HIP implementation)"
+            )
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        ex_args = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz]
+        lib.paged_attention.argtypes = ex_args + [vp]
+        lib.paged_attention.restype = ctypes.c_int
+        lib.paged_attention_ex.argtypes = ex_args + [i32, i32, vp]
+        lib.paged_attention_ex.restype = ctypes.c_int
+        lib.paged_attention_workspace_bytes.argtypes = [i32] * 7
+        lib.paged_attention_workspace_bytes.restype = sz
+        lib.paged_attention_workspace_bytes_ex.argtypes = [i32] * 9
+        lib.paged_attention_workspace_bytes_ex.restype = sz
+        lib.paged_attention_schedule.argtypes = [i32] * 7
+        lib.paged_attention_schedule.restype = ctypes.c_int
+        lib.paged_attention_check_metadata.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        lib.paged_attention_check_metadata.restype = ctypes.c_int
+        lib.paged_attention_last_error.argtypes = []
+        lib.paged_attention_last_error.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def last_error() -> str:
+    return load().paged_attention_last_error().decode()
+
+
+def _check(code: int) -> None:
+    if code != PA_OK:
+        raise PagedAttentionError(code, last_error())
+
+
+def workspace_bytes(batch, num_q_heads, num_kv_heads, query_len, head_dim, page_size, max_pages,
+                    schedule=SCHEDULE_AUTO, decode_split=0) -> int:
+    n = load().paged_attention_workspace_bytes_ex(batch, num_q_heads, num_kv_heads, query_len, head_dim,
+                                                  page_size, max_pages, schedule, decode_split)
+    if n == ctypes.c_size_t(-1).value:
+        raise PagedAttentionError(PA_ERR_INVALID, last_error())
+    return int(n)
+
+
+def schedule_for(batch, num_q_heads, num_kv_heads, query_len, head_dim, page_size, max_pages) -> int:
+    r = load().paged_attention_schedule(batch, num_q_heads, num_kv_heads, query_len, head_dim, page_size, max_pages)
+    if r < 0:
+        raise PagedAttentionError(r, last_error())
+    return int(r)
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream], device: torch.device) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return int(s.cuda_stream)
+
+
+def _require(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device: torch.device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+    if t.device != device:
+        raise ValueError(f"{name} must live on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def paged_attention(
+    query: torch.Tensor,
+    key_pages: torch.Tensor,
+    value_pages: torch.Tensor,
+    block_table: torch.Tensor,
+    context_lens: torch.Tensor,
+    page_size: int,
+    scale: Optional[float] = None,
+    causal: bool = True,
+    *,
+    out: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
+    schedule: int = SCHEDULE_AUTO,
+    decode_split: int = 0,
+    stream: Optional[torch.cuda.Stream] = None,
+) -> torch.Tensor:
+    """Paged attention on the GPU ("Week 3 Day 5: Paged FlashAttention", "Keep the Day 4 Interface").
+
+    query [B, H_q, L, D] bf16; key_pages / value_pages [num_pages, H_kv,
+    page_size, D] bf16; block_table [B, max_pages] int32; context_lens [B]
+    int32 -- all on one GPU. ``scale`` defaults to 1/sqrt(D). Returns
+    ``out`` [B, H_q, L, D] bf16 (allocated when not given). The call is
+    asynchronous on ``stream`` (default: the current stream).
+    """
+    dev = query.device
+    if dev.type != "cuda":
+        raise ValueError("query must be a GPU tensor")
+    _require(query, "query", torch.bfloat16, 4, dev)
+    _require(key_pages, "key_pages", torch.bfloat16, 4, dev)
+    _require(value_pages, "value_pages", torch.bfloat16, 4, dev)
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hq, L, D = query.shape
+    P, Hkv, ps, Dk = key_pages.shape
+    if tuple(value_pages.shape) != tuple(key_pages.shape):
+        raise ValueError("key_pages and value_pages must have the same shape")
+    if ps != page_size or Dk != D:
+        raise ValueError("page pool shape does not match page_size / head_dim")
+    if block_table.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_table and context_lens need one row per sequence")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty_like(query)
+    else:
+        _require(out, "out", torch.bfloat16, 4, dev)
+        if tuple(out.shape) != tuple(query.shape):
+            raise ValueError("out must have the query's shape")
+    need = workspace_bytes(B, Hq, Hkv, L, D, ps, max_pages, schedule, decode_split)
+    ws_ptr, ws_len = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the query's device")
+        ws_ptr, ws_len = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    lib = load()
+    rc = lib.paged_attention_ex(
+        query.data_ptr(), key_pages.data_ptr(), value_pages.data_ptr(), block_table.data_ptr(),
+        context_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, L, D, P, ps, max_pages, float(scale),
+        1 if causal else 0, ws_ptr, ws_len, int(schedule), int(decode_split), _stream_ptr(stream, dev),
+    )
+    _check(rc)
+    return out
+
+
+def check_metadata(block_table: torch.Tensor, context_lens: torch.Tensor, num_pages: int, page_size: int,
+                   query_len: int, causal: bool = True, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Debug check of the device-side metadata preconditions (synchronises the stream)."""
+    dev = block_table.device
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(context_lens, "context_lens", torch.int32, 1, dev)
+    rc = load().paged_attention_check_metadata(
+        block_table.data_ptr(), context_lens.data_ptr(), block_table.shape[0], block_table.shape[1],
+        num_pages, page_size, query_len, 1 if causal else 0, _stream_ptr(stream, dev),
+    )
+    _check(rc)

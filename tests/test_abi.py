@@ -1,0 +1,104 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments with an error code before any
+launch. The planning code is also built alone under ASan/UBSan."""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from paged_flashattention_kv_amd import native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attention.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(paged_attention\w*)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(native.LIB_PATH):
+        pytest.skip("library not built")
+    return native.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) == 7
+    assert sorted(native.EXPORTED) == names
+    raw = ctypes.CDLL(native.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _call(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, bt=FAKE + 0x300000, cl=FAKE + 0x400000,
+             out=FAKE + 0x500000, B=1, Hq=4, Hkv=2, L=1, D=128, P=8, ps=16, mp=4, scale=0.088,
+             causal=1, ws=None, wsb=0, sched=0, split=0)
+    a.update(kw)
+    return lib.paged_attention_ex(a["q"], a["k"], a["v"], a["bt"], a["cl"], a["out"], a["B"], a["Hq"], a["Hkv"],
+                                  a["L"], a["D"], a["P"], a["ps"], a["mp"], a["scale"], a["causal"], a["ws"],
+                                  a["wsb"], a["sched"], a["split"], None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(q=None), native.PA_ERR_INVALID),
+        (dict(out=None), native.PA_ERR_INVALID),
+        (dict(B=0), native.PA_ERR_INVALID),
+        (dict(Hq=3), native.PA_ERR_INVALID),
+        (dict(ps=0), native.PA_ERR_INVALID),
+        (dict(L=200), native.PA_ERR_INVALID),
+        (dict(causal=2), native.PA_ERR_INVALID),
+        (dict(scale=float("nan")), native.PA_ERR_INVALID),
+        (dict(D=64), native.PA_ERR_UNSUPPORTED),
+        (dict(sched=7), native.PA_ERR_INVALID),
+        (dict(L=5, sched=1), native.PA_ERR_INVALID),  # 10 rows > 8
+        (dict(sched=1, split=300), native.PA_ERR_INVALID),
+        (dict(out=FAKE), native.PA_ERR_INVALID),  # aliases the query
+        (dict(mp=400, ps=16, B=2, sched=1, split=256), native.PA_ERR_WORKSPACE),
+    ],
+)
+def test_invalid_arguments_return_codes(lib, kw, code):
+    assert _call(lib, **kw) == code
+    assert native.last_error() != ""
+
+
+def test_schedule_rule_and_workspace(lib):
+    assert native.schedule_for(64, 32, 8, 1, 128, 128, 33) == native.SCHEDULE_DECODE
+    assert native.schedule_for(64, 32, 8, 2, 128, 128, 33) == native.SCHEDULE_DECODE
+    assert native.schedule_for(64, 32, 8, 3, 128, 128, 33) == native.SCHEDULE_PREFILL
+    assert native.schedule_for(1, 8, 8, 8, 128, 128, 33) == native.SCHEDULE_DECODE
+    assert native.schedule_for(4, 32, 8, 2048, 128, 128, 16) == native.SCHEDULE_PREFILL
+    assert native.workspace_bytes(4, 32, 8, 2048, 128, 128, 16) == 0
+    # long decode: several splits, partials of (D + 2) floats per split and row
+    n = native.workspace_bytes(16, 32, 8, 1, 128, 16, 2048)
+    assert n >= 16 * 32 * 2 * 130 * 4
+    with pytest.raises(native.PagedAttentionError):
+        native.workspace_bytes(1, 3, 2, 1, 128, 16, 4)
+
+
+def test_host_planning_under_sanitizers(tmp_path):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ missing")
+    exe = str(tmp_path / "plan_check")
+    csrc = os.path.join(ROOT, "paged_flashattention_kv_amd", "csrc")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           f"-I{csrc}", os.path.join(ROOT, "tests", "host", "plan_check.cpp"), os.path.join(csrc, "pa_plan.cpp"),
+           "-o", exe]
+    subprocess.run(cmd, check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all passed" in r.stdout

@@ -1,0 +1,326 @@
+"""GPU parity: the HIP operator (through the C ABI) against the float64 oracle.
+
+Bar: max-abs error <= 2e-2 and mean-abs error <= 2e-3 of the bf16 output
+against the float64 oracle; indexing and visibility exactly (needle probes,
+page permutation and NaN poisoning are bit-identical or exact).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_flashattention_kv_amd import workloads as wl
+from tests.helpers import parity, run_gpu, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+DECODE, PREFILL = 1, 2
+
+
+def ref(p, **kw):
+    return oracle.paged_attention_ref(
+        p.query, p.key_pages, p.value_pages, p.block_table, p.context_lens, p.page_size, p.scale, p.causal, **kw
+    )
+
+
+def small(seed, B, Hq, Hkv, L, ctx, ps, causal=True, pool=None, poison=False, D=128):
+    return wl.make_problem(
+        seed=seed, batch=B, num_q_heads=Hq, num_kv_heads=Hkv, query_len=L, head_dim=D, page_size=ps,
+        context_lens=list(ctx), causal=causal, pool_pages=pool, poison=poison,
+    )
+
+
+def schedules_for(p):
+    """Both schedules when the decode one accepts the shape (debugging ladder)."""
+    rows = p.query_len * p.num_q_heads // p.num_kv_heads
+    return [DECODE, PREFILL] if rows <= 8 else [PREFILL]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_flashattention_kv_amd import native
+
+    native.load()
+
+
+# ------------------------------------------------------------------ configs
+
+
+def test_config_tiny_prefill():
+    p = wl.make_config("tiny_prefill")
+    say(f"tiny_prefill B=1 Hq=4 Hkv=2 L=13 ps=4 table={p.block_table.tolist()}")
+    want = ref(p)
+    got = run_gpu(p)
+    parity(got, want, "tiny_prefill")
+    # row 0 sees only key 0: the output is that key's value row, exactly
+    for h in range(4):
+        v0 = wl.bf16_bits_to_f32(p.value_pages[p.block_table[0, 0], h // 2, 0]).astype(np.float64)
+        assert np.array_equal(got[0, h, 0], v0)
+
+
+@pytest.fixture(scope="module")
+def decode_batch():
+    return wl.make_config("decode_batch")
+
+
+def test_config_decode_batch(decode_batch):
+    p = decode_batch
+    say(f"decode_batch B=64 ctx in [{p.context_lens.min()},{p.context_lens.max()}] ps=128")
+    want = ref(p)
+    parity(run_gpu(p), want, "decode_batch auto")
+
+
+@pytest.mark.parametrize("split", [256, 512, 2048, 4096])
+def test_decode_batch_split_lengths(decode_batch, split):
+    p = decode_batch
+    want = ref(p, pairs=[(b, h) for b in range(0, 64, 5) for h in (0, 13, 31)])
+    got = run_gpu(p, schedule=DECODE, decode_split=split)
+    sel = np.stack([got[b, h] for b in range(0, 64, 5) for h in (0, 13, 31)])
+    parity(sel, want, f"decode_batch split={split}")
+
+
+def test_config_long_prefill():
+    p = wl.make_config("long_prefill")
+    pairs = [(0, 0), (0, 31), (1, 5), (2, 18), (3, 27), (3, 3)]
+    say("long_prefill B=4 L=ctx=2048 ps=128 pairs", pairs)
+    want = ref(p, pairs=pairs)
+    got = run_gpu(p)
+    parity(np.stack([got[b, h] for b, h in pairs]), want, "long_prefill")
+    # causal row 0 of every head sees only key 0
+    for b in range(4):
+        for h in range(32):
+            v0 = wl.bf16_bits_to_f32(p.value_pages[p.block_table[b, 0], h // 4, 0]).astype(np.float64)
+            assert np.array_equal(got[b, h, 0], v0)
+
+
+def test_config_chunked_continuation():
+    p = wl.make_config("chunked_continuation")
+    say(f"chunked_continuation B=8 L=65 ctx={p.context_lens.tolist()}")
+    parity(run_gpu(p), ref(p), "chunked_continuation")
+
+
+@pytest.fixture(scope="module")
+def long_decode():
+    return wl.make_config("long_decode")
+
+
+def test_config_long_decode(long_decode):
+    p = long_decode
+    pairs = [(b, h) for b in (0, 7, 15) for h in range(32)]
+    say("long_decode B=16 ctx=32768 ps=16 (sampled rows)")
+    want = ref(p, pairs=pairs)
+    got = run_gpu(p)
+    parity(np.stack([got[b, h] for b, h in pairs]), want, "long_decode")
+
+
+# ------------------------------------------------------- needle probes
+
+
+def _plant_needle(p, b, h, l, t):
+    G = p.num_q_heads // p.num_kv_heads
+    phys = p.block_table[b, t // p.page_size]
+    k = wl.bf16_bits_to_f32(p.key_pages[phys, h // G, t % p.page_size])
+    p.query[b, h, l] = wl.f32_to_bf16_bits(8.0 * k)
+    return wl.bf16_bits_to_f32(p.value_pages[phys, h // G, t % p.page_size]).astype(np.float64)
+
+
+def _plant_hidden(p, b, h, l, slot_pos):
+    """q aimed at a slot that must stay invisible (past the context or causal bound)."""
+    G = p.num_q_heads // p.num_kv_heads
+    phys = p.block_table[b, slot_pos // p.page_size]
+    k = wl.bf16_bits_to_f32(p.key_pages[phys, h // G, slot_pos % p.page_size])
+    p.query[b, h, l] = wl.f32_to_bf16_bits(8.0 * k)
+    return wl.bf16_bits_to_f32(p.value_pages[phys, h // G, slot_pos % p.page_size]).astype(np.float64)
+
+
+def test_needles_decode_batch():
+    p = wl.make_config("decode_batch")
+    rng = np.random.default_rng(7)
+    needles, hidden = {}, {}
+    for b in range(64):
+        ctx = int(p.context_lens[b])
+        h = (5 * b) % 32
+        t = int(rng.integers(0, ctx))
+        needles[(b, h)] = _plant_needle(p, b, h, 0, t)
+        if ctx % p.page_size:  # an unused slot in the last page
+            h2 = (h + 16) % 32
+            hidden[(b, h2)] = _plant_hidden(p, b, h2, 0, ctx)
+    got = run_gpu(p)
+    for (b, h), v in needles.items():
+        assert np.max(np.abs(got[b, h, 0] - v)) <= 1e-2, (b, h)
+    for (b, h), v in hidden.items():
+        assert np.max(np.abs(got[b, h, 0] - v)) > 0.25, (b, h)
+    pairs = list(hidden.keys())[:16]
+    parity(np.stack([got[b, h] for b, h in pairs]), ref(p, pairs=pairs), "decode hidden needles")
+
+
+def test_needles_long_decode_page_crossing(long_decode):
+    p = wl.PagedProblem(**{**long_decode.__dict__, "query": long_decode.query.copy()})
+    needles = {}
+    targets = [0, 15, 16, 31, 32, 4095, 4096, 20000, 32767, 32752]
+    for i, t in enumerate(targets):
+        b, h = i % 16, (3 * i) % 32
+        needles[(b, h)] = _plant_needle(p, b, h, 0, t)
+    got = run_gpu(p)
+    for (b, h), v in needles.items():
+        assert np.max(np.abs(got[b, h, 0] - v)) <= 1e-2, (b, h)
+
+
+def test_needles_prefill_diagonal():
+    p = small(31, B=2, Hq=8, Hkv=2, L=300, ctx=(300, 421), ps=16)
+    needles, hidden = {}, {}
+    for b in range(2):
+        ctx = int(p.context_lens[b])
+        off = ctx - 300
+        for i, l in enumerate([0, 5, 63, 64, 127, 128, 200, 299]):
+            h = (i + 3 * b) % 8
+            last = l + off
+            t = last if i % 2 == 0 else (7 * l) % (last + 1)
+            needles[(b, h, l)] = _plant_needle(p, b, h, l, t)
+            if l < 299:
+                h2 = (h + 4) % 8
+                hidden[(b, h2, l)] = _plant_hidden(p, b, h2, l, last + 1)
+    got = run_gpu(p)
+    for (b, h, l), v in needles.items():
+        assert np.max(np.abs(got[b, h, l] - v)) <= 1e-2, (b, h, l)
+    for (b, h, l), v in hidden.items():
+        assert np.max(np.abs(got[b, h, l] - v)) > 0.25, (b, h, l)
+    parity(got, ref(p), "prefill needles")
+
+
+# ------------------------------------------------- fixtures and the grid
+
+
+def _fixture_cases():
+    with open(os.path.join(GOLDEN, "test_grid.json")) as f:
+        return json.load(f)["required_fixtures"]["cases"]
+
+
+@pytest.mark.parametrize("case", _fixture_cases(), ids=lambda c: c["name"])
+def test_required_fixtures(case):
+    ps, ctx, L = case["page_size"], case["context"], case["query_len"]
+    Hq, Hkv = (8, 2) if case["name"] == "gqa_group_of_4" else (4, 2)
+    p = small(41, B=2, Hq=Hq, Hkv=Hkv, L=L, ctx=(ctx, ctx + 37), ps=ps, poison=True)
+    want = ref(p)
+    for sch in schedules_for(p):
+        got = run_gpu(p, schedule=sch)
+        parity(got, want, f"{case['name']} schedule={sch}")
+
+
+def _grid():
+    with open(os.path.join(GOLDEN, "test_grid.json")) as f:
+        g = json.load(f)["week2_decode_grid"]
+    cases = []
+    for L in g["query_lens"] + [2]:
+        for ratio in g["gqa_ratios"]:
+            for ctx in g["contexts"]:
+                if ctx >= L:
+                    cases.append((L, ratio, ctx))
+    return cases
+
+
+@pytest.mark.parametrize("ps", [16, 128, 5])
+@pytest.mark.parametrize("L,ratio,ctx", _grid())
+def test_week2_grid(L, ratio, ctx, ps):
+    p = small(1000 + ctx + 13 * L + ratio + ps, B=2, Hq=2 * ratio, Hkv=2, L=L, ctx=(ctx, max(L, ctx - 7)),
+              ps=ps, poison=True)
+    want = ref(p)
+    for sch in schedules_for(p):
+        parity(run_gpu(p, schedule=sch), want, f"L={L} G={ratio} ctx={ctx} ps={ps} sch={sch}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("ps", [1, 3, 64, 256])
+def test_ragged_batch_odd_page_sizes(causal, ps):
+    p = small(77 + ps, B=5, Hq=6, Hkv=3, L=2, ctx=(2, 70, 129, 300, 555), ps=ps, causal=causal, poison=True)
+    want = ref(p)
+    for sch in schedules_for(p):
+        parity(run_gpu(p, schedule=sch), want, f"ragged ps={ps} causal={causal} sch={sch}")
+
+
+@pytest.mark.parametrize("L", [1, 33, 64, 65, 129, 200])
+def test_prefill_query_tiles_and_offsets(L):
+    p = small(90 + L, B=3, Hq=8, Hkv=2, L=L, ctx=(L, L + 100, L + 1000), ps=32, poison=True)
+    parity(run_gpu(p, schedule=PREFILL), ref(p), f"prefill L={L}")
+
+
+def test_noncausal_prefill():
+    p = small(95, B=2, Hq=4, Hkv=4, L=70, ctx=(30, 200), ps=16, causal=False, poison=True)
+    parity(run_gpu(p), ref(p), "noncausal prefill")
+
+
+# ------------------------------------------------------------ invariants
+
+
+def test_page_permutation_bit_identical_on_gpu():
+    for p in (small(51, B=3, Hq=8, Hkv=2, L=1, ctx=(100, 1000, 3000), ps=16),
+              small(52, B=2, Hq=8, Hkv=2, L=100, ctx=(100, 700), ps=64)):
+        q = wl.permute_pages(p, seed=3)
+        for sch in schedules_for(p):
+            a = run_gpu(p, schedule=sch)
+            b = run_gpu(q, schedule=sch)
+            assert np.array_equal(a, b), f"schedule {sch}"
+
+
+def test_poisoned_memory_bit_identical_on_gpu():
+    for kw in (dict(L=1, ctx=(77, 1000, 2001)), dict(L=40, ctx=(40, 333, 1000))):
+        clean = small(61, B=3, Hq=8, Hkv=2, ps=32, pool=100, **kw)
+        dirty = small(61, B=3, Hq=8, Hkv=2, ps=32, pool=100, poison=True, **kw)
+        for sch in schedules_for(clean):
+            a = run_gpu(clean, schedule=sch)
+            b = run_gpu(dirty, schedule=sch)
+            assert np.isfinite(b).all()
+            assert np.array_equal(a, b), f"schedule {sch}"
+
+
+def test_chunk_matches_tail_of_full_prefill():
+    ctx = 777
+    full = small(71, B=1, Hq=8, Hkv=2, L=ctx, ctx=(ctx,), ps=32)
+    got_full = run_gpu(full)
+    for L in (65, 2, 1):
+        chunk = wl.PagedProblem(**{**full.__dict__, "query": np.ascontiguousarray(full.query[:, :, ctx - L:, :])})
+        got = run_gpu(chunk)
+        parity(got, ref(chunk), f"chunk L={L}")
+        assert np.max(np.abs(got - got_full[:, :, ctx - L:, :])) <= 2e-2
+
+
+def test_output_guard_regions_untouched():
+    import torch
+    from paged_flashattention_kv_amd import native
+
+    p = small(81, B=3, Hq=8, Hkv=2, L=1, ctx=(50, 600, 3000), ps=16)
+    d = to_device(p)
+    n = p.query.size
+    for sch in (DECODE, PREFILL):
+        buf = torch.full((n + 2048,), 7.0, dtype=torch.bfloat16, device="cuda:0")
+        out = buf[1024:1024 + n].view(p.query.shape)
+        native.paged_attention(d["query"], d["key_pages"], d["value_pages"], d["block_table"], d["context_lens"],
+                               p.page_size, p.scale, True, out=out, schedule=sch)
+        torch.cuda.synchronize()
+        assert (buf[:1024] == 7.0).all() and (buf[1024 + n:] == 7.0).all()
+
+
+def test_metadata_check():
+    import torch
+    from paged_flashattention_kv_amd import native
+
+    p = small(82, B=2, Hq=4, Hkv=2, L=4, ctx=(10, 30), ps=4)
+    d = to_device(p)
+    native.check_metadata(d["block_table"], d["context_lens"], p.num_pages, p.page_size, 4)
+    bad = d["context_lens"].clone()
+    bad[1] = 3  # shorter than L under causal
+    with pytest.raises(native.PagedAttentionError):
+        native.check_metadata(d["block_table"], bad, p.num_pages, p.page_size, 4)
+    badt = d["block_table"].clone()
+    badt[0, 1] = p.num_pages
+    with pytest.raises(native.PagedAttentionError):
+        native.check_metadata(badt, d["context_lens"], p.num_pages, p.page_size, 4)
