@@ -27,7 +27,8 @@
  *     bf16 is stored as 16-bit words. All index arrays are int32.
  *   - The caller owns every buffer. The library allocates nothing, keeps no
  *     pointer after returning, and has no global state besides the
- *     thread-local error message. `out` must not alias any input.
+ *     thread-local error message and a per-device cache of how many decode
+ *     work items stay resident. `out` must not alias any input.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously; results are valid after the stream
  *     is synchronised.
@@ -58,7 +59,7 @@ enum {
 /* Which schedule runs. AUTO picks by query length (see paged_attention). */
 enum {
   PA_SCHEDULE_AUTO = 0,
-  PA_SCHEDULE_DECODE = 1,  /* short-query split-context schedule */
+  PA_SCHEDULE_DECODE = 1,  /* short-query schedule, context split over work items */
   PA_SCHEDULE_PREFILL = 2  /* long-query MFMA tiled schedule */
 };
 
@@ -77,9 +78,9 @@ enum {
  *   causal       0 or 1
  *   workspace    device scratch of at least
  *                paged_attention_workspace_bytes(...) bytes (may be NULL when
- *                that is 0); its contents need no initialisation and are
- *                garbage afterwards. Calls that share a workspace must be
- *                ordered on one stream.
+ *                that is 0: the prefill schedule needs none); its contents
+ *                need no initialisation and are garbage afterwards. Calls
+ *                that share a workspace must be ordered on one stream.
  *
  * Device-data preconditions (not checked; see
  * paged_attention_check_metadata): for every b,
@@ -101,14 +102,16 @@ int paged_attention(const void* query, const void* key_pages, const void* value_
                     void* stream);
 
 /*
- * paged_attention_ex -- paged_attention with the schedule and the decode
- * split length chosen by the caller (for tests of both schedules on one
- * input, "Week 3 Day 5", Task 3, and for tuning sweeps).
- *   schedule      PA_SCHEDULE_AUTO / _DECODE / _PREFILL. DECODE needs
- *                 query_len * num_q_heads / num_kv_heads <= 8.
- *   decode_split  keys per decode work item; 0 = automatic; otherwise a
- *                 multiple of 256 in [256, 65536] with
- *                 decode_split / page_size <= 2048.
+ * paged_attention_ex -- paged_attention with the schedule and the number of
+ * decode work items chosen by the caller (for tests of both schedules on
+ * one input, "Week 3 Day 5", Task 3, and for tuning sweeps).
+ *   schedule           PA_SCHEDULE_AUTO / _DECODE / _PREFILL. DECODE needs
+ *                      query_len * num_q_heads / num_kv_heads <= 8.
+ *   decode_work_items  the decode schedule splits the total K/V work (sum of
+ *                      context lengths times kv heads, in 64-key granules)
+ *                      evenly over this many work items; 0 = as many as the
+ *                      GPU keeps resident at once (at most 2048); otherwise
+ *                      1 .. 65536. Ignored by the prefill schedule.
  * Same arguments, preconditions and errors as paged_attention otherwise.
  */
 int paged_attention_ex(const void* query, const void* key_pages, const void* value_pages,
@@ -116,11 +119,12 @@ int paged_attention_ex(const void* query, const void* key_pages, const void* val
                        int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t query_len,
                        int32_t head_dim, int32_t num_pages, int32_t page_size, int32_t max_pages,
                        float scale, int32_t causal, void* workspace, size_t workspace_bytes,
-                       int32_t schedule, int32_t decode_split, void* stream);
+                       int32_t schedule, int32_t decode_work_items, void* stream);
 
 /*
  * Workspace bytes paged_attention (or paged_attention_ex with the same
- * schedule and decode_split) needs for these sizes; 0 when none is needed.
+ * schedule and decode_work_items) needs for these sizes; 0 when none is
+ * needed.
  * Returns (size_t)-1 if the sizes are invalid (see
  * paged_attention_last_error). Pure host arithmetic, no device access.
  */
@@ -129,7 +133,7 @@ size_t paged_attention_workspace_bytes(int32_t batch, int32_t num_q_heads, int32
                                        int32_t max_pages);
 size_t paged_attention_workspace_bytes_ex(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                           int32_t query_len, int32_t head_dim, int32_t page_size,
-                                          int32_t max_pages, int32_t schedule, int32_t decode_split);
+                                          int32_t max_pages, int32_t schedule, int32_t decode_work_items);
 
 /*
  * The schedule PA_SCHEDULE_AUTO resolves to for these sizes (DECODE or

@@ -8,33 +8,39 @@
 // merged through a common maximum) over paged K/V ("Week 3 Day 5: Paged
 // FlashAttention", Task 1: logical position -> block_table -> page slot).
 //
-// Schedule (HBM-bound; no matrix cores):
-//   work item = (split of the context, kv head, sequence), 256 threads.
-//   All query rows that read this kv head -- the GQA group times the query
-//   length, at most 8 rows -- are served by ONE pass over the split's keys,
-//   so every K/V byte is read from HBM once per kv head.
-//   Each wave walks 32-key tiles of the split (waves interleave tiles).
-//   Lane layout inside a tile: lane = 8 * kg + dc. Lane (kg, dc) holds keys
-//   kg, kg+8, kg+16, kg+24 of the tile and, for each, head dims
-//   [8dc, 8dc+8) and [64+8dc, 64+8dc+8): two 16-byte loads per key row, and
-//   one load instruction covers eight 128-byte row halves.
-//   q.k: packed bf16 dot products (v_dot2_f32_bf16), then a sum over the 8
-//   lanes of the key (DPP). The running maximum is shared by the whole wave
-//   (reduced per tile), so partial sums over the wave's lanes need no
-//   rescaling when they are combined at the end.
-//   Split end: wave partials are summed across lanes, then the 4 waves merge
-//   in LDS through a common maximum. With one split per sequence the result
-//   is normalised and stored directly; otherwise the split's (max, sum, acc)
-//   goes to the workspace and pa_decode_merge combines the splits.
+// Work division (HBM-bound; no matrix cores): the decode work is the sum of
+// the context lengths times the kv heads. It is cut into 64-key granules,
+// laid out segment by segment (segment = one (sequence, kv head) pair, in
+// sequence-major order), and the granule range is split evenly over a fixed
+// number of work items -- as many 256-thread work items as the GPU keeps
+// resident at once -- so every work item streams the same number of bytes
+// whatever the mix of context lengths. A work item walks its contiguous
+// range piece by piece (a piece = the part of one segment inside the range).
+// A piece that is a whole segment is normalised and stored directly; a
+// piece of a segment shared with other work items (at most the first and
+// the last piece of a range) leaves its (max, sum, acc) state in the
+// workspace, and pa_decode_merge combines those.
 //
-// Page translation ("Week 3 Day 5", Task 1): the split's block-table entries
-// are staged in LDS once. Aligned path (page_size % 32 == 0): a 32-key tile
-// lies inside one page, so its rows are one contiguous 8 KiB span found
-// with one table entry. Generic path: every key row is translated
-// separately (tiles that cross page boundaries, e.g. 16-token pages).
-// Keys at or past the split end are never loaded (their page may not
-// exist); their scores are forced to -inf by a separate mask ("Day 22: the
-// fused paged-attention kernel", "What I learned", item 2).
+// Inside a piece: all query rows that read this kv head -- the GQA group
+// times the query length, at most 8 rows -- are served by ONE pass over the
+// piece's keys, so every K/V byte is read from HBM once per kv head. Waves
+// interleave 16-key steps. Lane layout inside a step: lane = 8 * kg + dc;
+// lane (kg, dc) holds key kg (and kg + 8) and head dims [8dc, 8dc+8) and
+// [64+8dc, 64+8dc+8): two 16-byte loads per key row, one load instruction
+// covering eight 128-byte row halves. q.k: packed bf16 dot products
+// (v_dot2_f32_bf16) summed over the key's 8 lanes with DPP. The exponent
+// reference is shared by the whole wave, so wave partials combine without
+// rescaling; the 4 waves merge in LDS through a common maximum. Register
+// stages rotate so the next steps' K/V loads are in flight while a step is
+// computed.
+//
+// Page translation ("Week 3 Day 5", Task 1): the block-table entries of a
+// 2048-key window are staged in LDS. Aligned path (page_size % 32 == 0): a
+// step lies inside one page, found with one table entry. Generic path: every
+// key row is translated on its own (steps that cross page boundaries, e.g.
+// 16-token pages). Keys past the piece end are never loaded from their own
+// (possibly missing) page; their scores are forced to -inf by a separate
+// mask ("Day 22: the fused paged-attention kernel", "What I learned", 2).
 
 #include "pa_device.h"
 #include "pa_kernels.h"
@@ -45,7 +51,25 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kTile = 32;
+// Keys each lane holds per step (a wave step covers 8 * kTK keys), and the
+// number of register stages per wave: the K/V loads of the next
+// kStages - 1 steps are issued before the current step is computed.
+#ifndef PA_DECODE_TK
+#define PA_DECODE_TK 2
+#endif
+constexpr int kTK = PA_DECODE_TK;
+#ifndef PA_DECODE_STAGES
+#define PA_DECODE_STAGES 3
+#endif
+constexpr int kStages = PA_DECODE_STAGES;
+constexpr int kStep = 8 * kTK;
+// The exponent reference of a row moves only when a tile's maximum exceeds it
+// by more than kTau (log2 units), so weights stay <= 2^kTau and the common
+// case needs no rescale of the accumulators.
+constexpr float kTau = 8.0f;
+
+constexpr int kGran = 64;    // keys per granule: work ranges start and end on granules
+constexpr int kWindow = 2048;  // keys per block-table staging window
 
 struct DecodeArgs {
   const uint16_t* query;
@@ -54,46 +78,168 @@ struct DecodeArgs {
   const int32_t* block_table;
   const int32_t* context_lens;
   uint16_t* out;
-  float* ws_acc;
-  float* ws_ml;
-  int num_q_heads, num_kv_heads, query_len, group, rows;
+  int64_t* ws_pref;  // [batch + 1] granule prefix over sequences (written by work item 0)
+  float* ws_ml;      // [work_items][2][rows][2]   partial (reference max, sum)
+  float* ws_acc;     // [work_items][2][rows][128] partial unnormalised outputs
+  int batch, num_q_heads, num_kv_heads, query_len, group, rows;
   int page_size, ps_log2, max_pages;
-  int split_len, n_split;
+  int work_items;
   float c;  // scale * log2(e)
   int causal;
 };
 
 __device__ __forceinline__ int div_ps(int s, int ps, int ps_log2) { return ps_log2 >= 0 ? (s >> ps_log2) : s / ps; }
 
-template <int ROWS, bool ALIGNED, bool DIRECT>
-__global__ void __launch_bounds__(kThreads) pa_decode_split(DecodeArgs a) {
-  extern __shared__ int32_t lds_bt[];
-  __shared__ float lds_m[kWaves][ROWS];
-  __shared__ float lds_l[kWaves][ROWS];
-  __shared__ float lds_acc[kWaves][ROWS][128];
+struct Stage {
+  u32x4_t k[kTK][2];
+  u32x4_t v[kTK][2];
+};
 
+struct Pager {
+  const uint16_t* kpages;
+  const uint16_t* vpages;
+  const int32_t* lds_bt;  // block-table entries of the split, from logical page lp0
+  size_t page_stride, head_off;
+  int lp0, s0, s1, page_size, ps_log2;
+  int kg, dc;
+};
+
+// Page-translating load of one step: keys t0 + kg + 8i (i < kTK), dims
+// [8dc, 8dc+8) and [64+8dc, 64+8dc+8). Keys at or past the split end are
+// redirected to the split's first key (always a valid row) so every load is
+// unconditional; their scores are masked to -inf and their weight is 0.
+template <bool ALIGNED>
+__device__ __forceinline__ void load_stage(const Pager& g, int t0, Stage& st) {
+  size_t row[kTK];
+  if (ALIGNED) {
+    // page_size % 32 == 0 and t0 % 8kTK == 0: the step lies inside one page.
+    // A step wholly past the split end reads the split's first page instead.
+    const int tb = t0 < g.s1 ? t0 : g.s0;
+    const int lp = div_ps(tb, g.page_size, g.ps_log2);
+    const size_t base = (size_t)g.lds_bt[lp - g.lp0] * g.page_stride + g.head_off +
+                        (size_t)(tb - lp * g.page_size) * 128;
+#pragma unroll
+    for (int i = 0; i < kTK; ++i) {
+      const int key = t0 + g.kg + 8 * i;
+      row[i] = key < g.s1 ? base + (size_t)(g.kg + 8 * i) * 128 : base;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kTK; ++i) {
+      int key = t0 + g.kg + 8 * i;
+      key = key < g.s1 ? key : g.s0;
+      const int lp = div_ps(key, g.page_size, g.ps_log2);
+      row[i] = (size_t)g.lds_bt[lp - g.lp0] * g.page_stride + g.head_off + (size_t)(key - lp * g.page_size) * 128;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kTK; ++i) {
+    st.k[i][0] = *reinterpret_cast<const u32x4_t*>(g.kpages + row[i] + g.dc * 8);
+    st.k[i][1] = *reinterpret_cast<const u32x4_t*>(g.kpages + row[i] + 64 + g.dc * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < kTK; ++i) {
+    st.v[i][0] = *reinterpret_cast<const u32x4_t*>(g.vpages + row[i] + g.dc * 8);
+    st.v[i][1] = *reinterpret_cast<const u32x4_t*>(g.vpages + row[i] + 64 + g.dc * 8);
+  }
+}
+
+template <int ROWS>
+struct RowState {
+  float m[ROWS];     // exponent reference (wave-uniform), log2 units
+  float lsum[ROWS];  // this lane's share of the row sum
+  float acc[ROWS][16];
+};
+
+template <int ROWS>
+__device__ __forceinline__ void compute_stage(const Stage& st, int t0, int s1, const uint32_t (&q)[ROWS][8],
+                                              const int (&last)[ROWS], int min_last, float c, int kg,
+                                              RowState<ROWS>& rs) {
+  // scores (raw q.k): lane-partial bf16 dot products, summed over the key's 8 lanes
+  float s[ROWS][kTK];
+#pragma unroll
+  for (int i = 0; i < kTK; ++i) {
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      float d = 0.f;
+      d = dot2_bf16(q[r][0], st.k[i][0].x, d);
+      d = dot2_bf16(q[r][1], st.k[i][0].y, d);
+      d = dot2_bf16(q[r][2], st.k[i][0].z, d);
+      d = dot2_bf16(q[r][3], st.k[i][0].w, d);
+      d = dot2_bf16(q[r][4], st.k[i][1].x, d);
+      d = dot2_bf16(q[r][5], st.k[i][1].y, d);
+      d = dot2_bf16(q[r][6], st.k[i][1].z, d);
+      d = dot2_bf16(q[r][7], st.k[i][1].w, d);
+      s[r][i] = sum_lanes8(d);
+    }
+  }
+  // visibility: past the split end, or hidden by the causal rule (separate from the load)
+  if (t0 + kStep > s1 || t0 + kStep - 1 > min_last) {
+#pragma unroll
+    for (int i = 0; i < kTK; ++i) {
+      const int key = t0 + kg + 8 * i;
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r)
+        if (!(key < s1 && key <= last[r])) s[r][i] = -INFINITY;
+    }
+  }
+  // online softmax: the step maximum moves the reference only past the threshold
+  float p[ROWS][kTK];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    float tmax = s[r][0];
+#pragma unroll
+    for (int i = 1; i < kTK; ++i) tmax = fmaxf(tmax, s[r][i]);
+    tmax = max_stride8(tmax) * c;
+    if (tmax > rs.m[r] + kTau) {  // uniform across the wave
+      const float alpha = fast_exp2(rs.m[r] - tmax);  // 0 when the old reference is -inf
+      rs.m[r] = tmax;
+      rs.lsum[r] *= alpha;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) rs.acc[r][j] *= alpha;
+    }
+    const float mref = rs.m[r] == -INFINITY ? 0.f : rs.m[r];
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < kTK; ++i) {
+      p[r][i] = fast_exp2(fmaf(s[r][i], c, -mref));
+      ps += p[r][i];
+    }
+    rs.lsum[r] += ps;
+  }
+  // weighted values, fp32
+#pragma unroll
+  for (int i = 0; i < kTK; ++i) {
+    const uint32_t w[8] = {st.v[i][0].x, st.v[i][0].y, st.v[i][0].z, st.v[i][0].w,
+                           st.v[i][1].x, st.v[i][1].y, st.v[i][1].z, st.v[i][1].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        rs.acc[r][2 * j] = fmaf(p[r][i], lo, rs.acc[r][2 * j]);
+        rs.acc[r][2 * j + 1] = fmaf(p[r][i], hi, rs.acc[r][2 * j + 1]);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ int64_t n_gran(int ctx) { return (ctx + kGran - 1) / kGran; }
+
+// Work item w covers granules [w * total / work_items, (w + 1) * total / work_items).
+__device__ __forceinline__ int64_t gran_begin(int64_t w, int64_t total, int64_t items) { return w * total / items; }
+
+// One piece: keys [k0, k1) of segment (b, kvh). Leaves the merged state in
+// LDS-free registers of the caller's work item and stores it.
+template <int ROWS, bool ALIGNED>
+__device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_bt, float (*lds_m)[ROWS],
+                                             float (*lds_l)[ROWS], float (*lds_acc)[ROWS][128], int b, int kvh,
+                                             int ctx, int k0, int k1, bool direct, int slot) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int kg = lane >> 3;
   const int dc = lane & 7;
-
-  int wid = blockIdx.x;
-  const int split = wid % a.n_split;
-  wid /= a.n_split;
-  const int kvh = wid % a.num_kv_heads;
-  const int b = wid / a.num_kv_heads;
-
-  const int ctx = a.context_lens[b];
-  const int s0 = split * a.split_len;
-  if (s0 >= ctx) return;  // this split holds no key of the sequence
-  const int s1 = min(s0 + a.split_len, ctx);
-
-  // Stage the split's block-table entries.
-  const int lp0 = div_ps(s0, a.page_size, a.ps_log2);
-  const int nbt = div_ps(s1 - 1, a.page_size, a.ps_log2) - lp0 + 1;
-  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages + lp0;
-  for (int i = tid; i < nbt; i += kThreads) lds_bt[i] = bt_row[i];
 
   // Query rows of this kv head: row r -> q head kvh*group + r / L, position r % L.
   uint32_t q[ROWS][8];
@@ -118,154 +264,94 @@ __global__ void __launch_bounds__(kThreads) pa_decode_split(DecodeArgs a) {
   int min_last = ctx - 1;
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) min_last = min(min_last, last[r]);
-  __syncthreads();
 
-  float m[ROWS], lsum[ROWS], acc[ROWS][16];
+  RowState<ROWS> rs;
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    m[r] = -INFINITY;
-    lsum[r] = 0.f;
+    rs.m[r] = -INFINITY;
+    rs.lsum[r] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[r][j] = 0.f;
+    for (int j = 0; j < 16; ++j) rs.acc[r][j] = 0.f;
   }
 
-  const size_t head_stride = (size_t)a.page_size * 128;  // elements between kv heads of a page
-  const size_t page_stride = head_stride * a.num_kv_heads;
-  const size_t head_off = (size_t)kvh * head_stride;
+  Pager g;
+  g.kpages = a.kpages;
+  g.vpages = a.vpages;
+  g.lds_bt = lds_bt;
+  g.page_stride = (size_t)a.page_size * 128 * a.num_kv_heads;
+  g.head_off = (size_t)kvh * a.page_size * 128;
+  g.page_size = a.page_size;
+  g.ps_log2 = a.ps_log2;
+  g.kg = kg;
+  g.dc = dc;
+  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
 
-  for (int t0 = s0 + wave * kTile; t0 < s1; t0 += kWaves * kTile) {
-    // ---- page-translating load of the tile's K and V rows (registers) ----
-    u32x4_t kr[4][2], vr[4][2];
-    size_t row_off[4];
-    bool ok[4];
-    if (ALIGNED) {
-      const int lp = div_ps(t0, a.page_size, a.ps_log2);
-      const int slot0 = t0 - lp * a.page_size;
-      const size_t base = (size_t)lds_bt[lp - lp0] * page_stride + head_off + (size_t)slot0 * 128;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        row_off[i] = base + (size_t)(kg + 8 * i) * 128;
-        ok[i] = t0 + kg + 8 * i < s1;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = t0 + kg + 8 * i;
-        ok[i] = s < s1;
-        const int sc = ok[i] ? s : s0;
-        const int lp = div_ps(sc, a.page_size, a.ps_log2);
-        const int slot = sc - lp * a.page_size;
-        row_off[i] = (size_t)lds_bt[lp - lp0] * page_stride + head_off + (size_t)slot * 128;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (ok[i]) {
-        kr[i][0] = *reinterpret_cast<const u32x4_t*>(a.kpages + row_off[i] + dc * 8);
-        kr[i][1] = *reinterpret_cast<const u32x4_t*>(a.kpages + row_off[i] + 64 + dc * 8);
-      } else {
-        kr[i][0] = u32x4_t{0u, 0u, 0u, 0u};
-        kr[i][1] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (ok[i]) {
-        vr[i][0] = *reinterpret_cast<const u32x4_t*>(a.vpages + row_off[i] + dc * 8);
-        vr[i][1] = *reinterpret_cast<const u32x4_t*>(a.vpages + row_off[i] + 64 + dc * 8);
-      } else {
-        vr[i][0] = u32x4_t{0u, 0u, 0u, 0u};
-        vr[i][1] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
+  for (int ka = k0; ka < k1; ka += kWindow) {
+    const int kb = min(ka + kWindow, k1);
+    // stage the window's block-table entries
+    const int lp0 = div_ps(ka, a.page_size, a.ps_log2);
+    const int nbt = div_ps(kb - 1, a.page_size, a.ps_log2) - lp0 + 1;
+    __syncthreads();  // the previous window (or piece) is done with lds_bt
+    for (int i = tid; i < nbt; i += kThreads) lds_bt[i] = bt_row[lp0 + i];
+    __syncthreads();
+    g.lp0 = lp0;
+    g.s0 = ka;
+    g.s1 = kb;
 
-    // ---- scores: lane-partial bf16 dot products, summed over the key's 8 lanes ----
-    float s[ROWS][4];
+    // Each wave walks steps ka + wave*kStep, + kWaves*kStep, ...; kStages
+    // register stages rotate so kStages - 1 steps of loads are in flight
+    // while the oldest landed step is computed. Every stage load is issued
+    // unconditionally (steps past the window re-read its first row), which
+    // keeps the number of outstanding loads the same on every path, so the
+    // waits before each step cover only that step's own loads.
+    constexpr int kStride = kWaves * kStep;
+    int t = ka + wave * kStep;
+    if (t < kb) {
+      Stage st[kStages];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kStages - 1; ++i) load_stage<ALIGNED>(g, t + i * kStride, st[i]);
+      bool done = false;
+      while (!done) {
 #pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        float d = 0.f;
-        d = dot2_bf16(q[r][0], kr[i][0].x, d);
-        d = dot2_bf16(q[r][1], kr[i][0].y, d);
-        d = dot2_bf16(q[r][2], kr[i][0].z, d);
-        d = dot2_bf16(q[r][3], kr[i][0].w, d);
-        d = dot2_bf16(q[r][4], kr[i][1].x, d);
-        d = dot2_bf16(q[r][5], kr[i][1].y, d);
-        d = dot2_bf16(q[r][6], kr[i][1].z, d);
-        d = dot2_bf16(q[r][7], kr[i][1].w, d);
-        s[r][i] = sum_lanes8(d) * a.c;
+        for (int j = 0; j < kStages; ++j) {
+          load_stage<ALIGNED>(g, t + (kStages - 1) * kStride, st[(j + kStages - 1) % kStages]);
+          compute_stage<ROWS>(st[j], t, kb, q, last, min_last, a.c, kg, rs);
+          t += kStride;
+          if (t >= kb) {
+            done = true;
+            break;
+          }
+        }
       }
-    }
-    // ---- visibility: past the split end, or hidden by the causal rule ----
-    if (t0 + kTile > s1 || t0 + kTile - 1 > min_last) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = t0 + kg + 8 * i;
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r)
-          if (!(key < s1 && key <= last[r])) s[r][i] = -INFINITY;
-      }
-    }
-    // ---- online softmax with a wave-wide running maximum ----
-    float p[ROWS][4];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      float tmax = fmaxf(fmaxf(s[r][0], s[r][1]), fmaxf(s[r][2], s[r][3]));
-      tmax = max_stride8(tmax);
-      const float m_new = fmaxf(m[r], tmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m[r] - m_use);
-      m[r] = m_new;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[r][i] = fast_exp2(s[r][i] - m_use);
-      lsum[r] = lsum[r] * alpha + ((p[r][0] + p[r][1]) + (p[r][2] + p[r][3]));
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[r][j] *= alpha;
-    }
-    // ---- weighted values ----
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v[16];
-      const uint32_t w[8] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w,
-                             vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        v[2 * j] = bf16_lo(w[j]);
-        v[2 * j + 1] = bf16_hi(w[j]);
-      }
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[r][j] = fmaf(p[r][i], v[j], acc[r][j]);
     }
   }
 
-  // ---- merge: lanes of the wave (same maximum), then the 4 waves in LDS ----
+  // ---- merge: lanes of the wave (same reference), then the 4 waves in LDS ----
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    lsum[r] = sum_stride8(lsum[r]);  // over the 8 key groups of the wave
+    rs.lsum[r] = sum_stride8(rs.lsum[r]);  // over the 8 key groups of the wave
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[r][j] = sum_stride8(acc[r][j]);
+    for (int j = 0; j < 16; ++j) rs.acc[r][j] = sum_stride8(rs.acc[r][j]);
   }
   if (kg == 0) {
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        lds_acc[wave][r][dc * 8 + j] = acc[r][j];
-        lds_acc[wave][r][64 + dc * 8 + j] = acc[r][8 + j];
+        lds_acc[wave][r][dc * 8 + j] = rs.acc[r][j];
+        lds_acc[wave][r][64 + dc * 8 + j] = rs.acc[r][8 + j];
       }
     }
     if (dc == 0) {
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
-        lds_m[wave][r] = m[r];
-        lds_l[wave][r] = lsum[r];
+        lds_m[wave][r] = rs.m[r];
+        lds_l[wave][r] = rs.lsum[r];
       }
     }
   }
   __syncthreads();
+  const size_t part = ((size_t)blockIdx.x * 2 + slot) * a.rows;
   for (int idx = tid; idx < a.rows * 128; idx += kThreads) {
     const int r = idx >> 7;
     const int d = idx & 127;
@@ -283,57 +369,168 @@ __global__ void __launch_bounds__(kThreads) pa_decode_split(DecodeArgs a) {
       den = fmaf(f, lds_l[w][r], den);
       num = fmaf(f, lds_acc[w][r][d], num);
     }
-    const int h = kvh * a.group + r / a.query_len;
-    const int l = r % a.query_len;
-    const size_t orow = ((size_t)b * a.num_q_heads + h) * a.query_len + l;
-    if (DIRECT) {
+    if (direct) {
+      const int h = kvh * a.group + r / a.query_len;
+      const int l = r % a.query_len;
+      const size_t orow = ((size_t)b * a.num_q_heads + h) * a.query_len + l;
       a.out[orow * 128 + d] = to_bf16(num / den);
     } else {
-      a.ws_acc[(orow * a.n_split + split) * 128 + d] = num;
+      a.ws_acc[(part + r) * 128 + d] = num;
       if (d == 0) {
-        a.ws_ml[(orow * a.n_split + split) * 2 + 0] = M;
-        a.ws_ml[(orow * a.n_split + split) * 2 + 1] = den;
+        a.ws_ml[(part + r) * 2 + 0] = M;
+        a.ws_ml[(part + r) * 2 + 1] = den;
       }
     }
   }
 }
 
-// Combines the per-split partial states of one output row ("Week 2 Day 5",
-// Task 2: common maximum, one rescale factor per partial, one denominator,
-// one thread per head dimension). Splits whose state is empty (maximum
-// -inf) contribute nothing.
-__global__ void __launch_bounds__(128) pa_decode_merge(DecodeArgs a) {
-  const int orow = blockIdx.x;
-  const int d = threadIdx.x;
-  const int b = orow / (a.num_q_heads * a.query_len);
-  const int ctx = a.context_lens[b];
-  const int n = (ctx + a.split_len - 1) / a.split_len;
-  const float* ml = a.ws_ml + (size_t)orow * a.n_split * 2;
-  const float* acc = a.ws_acc + (size_t)orow * a.n_split * 128 + d;
-  float M = -INFINITY;
-  for (int j = 0; j < n; ++j) M = fmaxf(M, ml[2 * j]);
-  float den = 0.f, num = 0.f;
-  for (int j = 0; j < n; ++j) {
-    const float mj = ml[2 * j];
-    if (mj == -INFINITY) continue;
-    const float f = fast_exp2(mj - M);
-    den = fmaf(f, ml[2 * j + 1], den);
-    num = fmaf(f, acc[(size_t)j * 128], num);
+template <int ROWS, bool ALIGNED>
+__global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
+  extern __shared__ int32_t lds_bt[];
+  __shared__ float lds_m[kWaves][ROWS];
+  __shared__ float lds_l[kWaves][ROWS];
+  __shared__ float lds_acc[kWaves][ROWS][128];
+  __shared__ int64_t lds_scan[kThreads];
+  __shared__ int64_t lds_start[2];  // (sequence holding the first granule, its granule prefix)
+
+  const int tid = threadIdx.x;
+  // ---- granule prefix over sequences: thread t sums a contiguous chunk ----
+  const int chunk = (a.batch + kThreads - 1) / kThreads;
+  const int c0 = min(a.batch, tid * chunk), c1 = min(a.batch, c0 + chunk);
+  int64_t mine = 0;
+  for (int b = c0; b < c1; ++b) mine += n_gran(a.context_lens[b]);
+  lds_scan[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan
+    const int64_t v = tid >= off ? lds_scan[tid - off] : 0;
+    __syncthreads();
+    lds_scan[tid] += v;
+    __syncthreads();
   }
-  a.out[(size_t)orow * 128 + d] = to_bf16(num / den);
+  const int64_t total_b = lds_scan[kThreads - 1];  // granules per kv head, all sequences
+  const int64_t total = total_b * a.num_kv_heads;
+  const int64_t excl = lds_scan[tid] - mine;
+  const int64_t w = blockIdx.x;
+  const int64_t G0 = gran_begin(w, total, a.work_items);
+  const int64_t G1 = gran_begin(w + 1, total, a.work_items);
+  {
+    // which sequence holds granule G0 (and write the prefix once for the merge)
+    int64_t pref = excl;
+    for (int b = c0; b < c1; ++b) {
+      const int64_t ng = n_gran(a.context_lens[b]);
+      if (blockIdx.x == 0) a.ws_pref[b] = pref;
+      if (G0 >= pref * a.num_kv_heads && G0 < (pref + ng) * a.num_kv_heads) {
+        lds_start[0] = b;
+        lds_start[1] = pref;
+      }
+      pref += ng;
+    }
+    if (blockIdx.x == 0 && tid == kThreads - 1) a.ws_pref[a.batch] = total_b;
+  }
+  __syncthreads();
+  if (G0 >= G1) return;  // no work for this item (uniform)
+
+  int b = (int)lds_start[0];
+  int64_t pref = lds_start[1];
+  int64_t G = G0;
+  int nth = 0;
+  while (G < G1) {
+    const int ctx = a.context_lens[b];
+    const int64_t ng = n_gran(ctx);
+    const int64_t base = pref * a.num_kv_heads;  // first granule of sequence b
+    const int kvh = (int)((G - base) / ng);
+    const int64_t S = base + kvh * ng, E = S + ng;
+    const int64_t gend = G1 < E ? G1 : E;
+    const int k0 = (int)((G - S) * kGran);
+    const int k1 = (int)min((gend - S) * kGran, (int64_t)ctx);
+    const bool direct = G == S && gend == E;
+    decode_piece<ROWS, ALIGNED>(a, lds_bt, lds_m, lds_l, lds_acc, b, kvh, ctx, k0, k1, direct, nth == 0 ? 0 : 1);
+    G = gend;
+    ++nth;
+    if (G == base + (int64_t)a.num_kv_heads * ng) {  // past the last kv head of sequence b
+      ++b;
+      pref += ng;
+    }
+  }
 }
 
-template <int ROWS, bool ALIGNED, bool DIRECT>
-hipError_t launch_split(const DecodeArgs& a, int64_t grid, size_t lds_bytes, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_decode_split<ROWS, ALIGNED, DIRECT>), dim3((unsigned)grid), dim3(kThreads), lds_bytes,
+// Combines the partial states of segments shared by several work items
+// ("Week 2 Day 5", Task 2: common maximum, one rescale factor per partial,
+// one denominator, the head dimensions in parallel). One wave per output
+// row; every lane owns two head dims. The work items covering the row's
+// segment and the slot each used are recomputed from the same even split of
+// the granules. Partials with maximum -inf (no visible key) contribute 0.
+__global__ void __launch_bounds__(64) pa_decode_merge(DecodeArgs a) {
+  const int orow = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int L = a.query_len;
+  const int b = orow / (a.num_q_heads * L);
+  const int h = (orow / L) % a.num_q_heads;
+  const int l = orow % L;
+  const int kvh = h / a.group;
+  const int r = (h - kvh * a.group) * L + l;
+  const int64_t total = a.ws_pref[a.batch] * a.num_kv_heads;
+  const int64_t ng = n_gran(a.context_lens[b]);
+  const int64_t S = a.ws_pref[b] * a.num_kv_heads + kvh * ng, E = S + ng;
+  const int64_t P = a.work_items;
+  const int64_t wf = ((S + 1) * P - 1) / total;  // work item holding granule S
+  const int64_t wl = (E * P - 1) / total;        // work item holding granule E - 1
+  if (wf == wl) return;                          // whole segment in one item: stored directly
+  float M = -INFINITY;
+  for (int64_t w = wf; w <= wl; ++w) {
+    const int64_t gw = gran_begin(w, total, P);
+    if (gw == gran_begin(w + 1, total, P)) continue;  // empty work item
+    const size_t part = ((size_t)w * 2 + (gw >= S ? 0 : 1)) * a.rows + r;
+    M = fmaxf(M, a.ws_ml[part * 2]);
+  }
+  float den = 0.f, n0 = 0.f, n1 = 0.f;
+  for (int64_t w = wf; w <= wl; ++w) {
+    const int64_t gw = gran_begin(w, total, P);
+    if (gw == gran_begin(w + 1, total, P)) continue;
+    const size_t part = ((size_t)w * 2 + (gw >= S ? 0 : 1)) * a.rows + r;
+    const float mj = a.ws_ml[part * 2];
+    const float f = mj == -INFINITY ? 0.f : fast_exp2(mj - M);
+    const f32x2_t v = *reinterpret_cast<const f32x2_t*>(a.ws_acc + part * 128 + 2 * lane);
+    den = fmaf(f, a.ws_ml[part * 2 + 1], den);
+    n0 = fmaf(f, v.x, n0);
+    n1 = fmaf(f, v.y, n1);
+  }
+  const float inv = 1.f / den;
+  *reinterpret_cast<uint32_t*>(a.out + (size_t)orow * 128 + 2 * lane) = pack_bf16x2(n0 * inv, n1 * inv);
+}
+
+template <int ROWS, bool ALIGNED>
+hipError_t launch_work(const DecodeArgs& a, size_t lds_bytes, hipStream_t stream) {
+  hipLaunchKernelGGL((pa_decode_work<ROWS, ALIGNED>), dim3((unsigned)a.work_items), dim3(kThreads), lds_bytes,
                      stream, a);
   return hipGetLastError();
 }
 
+// Work items the GPU keeps resident for one kernel instance (cached per device).
+template <int ROWS, bool ALIGNED>
+int resident_items(size_t lds_bytes) {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] > 0) return cache[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)pa_decode_work<ROWS, ALIGNED>, kThreads,
+                                                   lds_bytes) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  const int n = cus * per_cu;
+  cache[dev] = n;
+  return n;
+}
+
 template <int ROWS>
-hipError_t launch_rows(const DecodeArgs& a, bool aligned, bool direct, int64_t grid, size_t lds, hipStream_t st) {
-  if (aligned) return direct ? launch_split<ROWS, true, true>(a, grid, lds, st) : launch_split<ROWS, true, false>(a, grid, lds, st);
-  return direct ? launch_split<ROWS, false, true>(a, grid, lds, st) : launch_split<ROWS, false, false>(a, grid, lds, st);
+hipError_t launch_rows(DecodeArgs& a, bool aligned, int requested, int cap, size_t lds, hipStream_t st) {
+  if (aligned) {
+    a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, true>(lds));
+    return launch_work<ROWS, true>(a, lds, st);
+  }
+  a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, false>(lds));
+  return launch_work<ROWS, false>(a, lds, st);
 }
 
 }  // namespace
@@ -347,8 +544,10 @@ hipError_t launch_decode(const KernelArgs& k, const Plan& p, hipStream_t stream)
   a.context_lens = k.context_lens;
   a.out = static_cast<uint16_t*>(k.out);
   char* ws = static_cast<char*>(k.workspace);
-  a.ws_acc = p.direct ? nullptr : reinterpret_cast<float*>(ws + p.ws_acc_offset);
-  a.ws_ml = p.direct ? nullptr : reinterpret_cast<float*>(ws + p.ws_ml_offset);
+  a.ws_pref = reinterpret_cast<int64_t*>(ws + p.ws_pref_offset);
+  a.ws_ml = reinterpret_cast<float*>(ws + p.ws_ml_offset);
+  a.ws_acc = reinterpret_cast<float*>(ws + p.ws_acc_offset);
+  a.batch = k.batch;
   a.num_q_heads = k.num_q_heads;
   a.num_kv_heads = k.num_kv_heads;
   a.query_len = k.query_len;
@@ -357,21 +556,19 @@ hipError_t launch_decode(const KernelArgs& k, const Plan& p, hipStream_t stream)
   a.page_size = k.page_size;
   a.ps_log2 = p.ps_log2;
   a.max_pages = k.max_pages;
-  a.split_len = p.split_len;
-  a.n_split = p.n_split;
   a.c = k.scale * kLog2e;
   a.causal = k.causal;
   const size_t lds = (size_t)p.bt_entries * sizeof(int32_t);
   hipError_t e;
   switch (p.rows_pad) {
-    case 1: e = launch_rows<1>(a, p.aligned, p.direct, p.num_work, lds, stream); break;
-    case 2: e = launch_rows<2>(a, p.aligned, p.direct, p.num_work, lds, stream); break;
-    case 4: e = launch_rows<4>(a, p.aligned, p.direct, p.num_work, lds, stream); break;
-    default: e = launch_rows<8>(a, p.aligned, p.direct, p.num_work, lds, stream); break;
+    case 1: e = launch_rows<1>(a, p.aligned, p.work_items, p.work_cap, lds, stream); break;
+    case 2: e = launch_rows<2>(a, p.aligned, p.work_items, p.work_cap, lds, stream); break;
+    case 4: e = launch_rows<4>(a, p.aligned, p.work_items, p.work_cap, lds, stream); break;
+    default: e = launch_rows<8>(a, p.aligned, p.work_items, p.work_cap, lds, stream); break;
   }
-  if (e != hipSuccess || p.direct) return e;
+  if (e != hipSuccess) return e;
   const int64_t nrows = (int64_t)k.batch * k.num_q_heads * k.query_len;
-  hipLaunchKernelGGL(pa_decode_merge, dim3((unsigned)nrows), dim3(128), 0, stream, a);
+  hipLaunchKernelGGL(pa_decode_merge, dim3((unsigned)nrows), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -25,19 +25,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 }  // namespace
 
-int auto_decode_split(int64_t batch, int64_t num_kv_heads, int64_t max_ctx, int64_t page_size) {
-  // Smallest split (512, 1024, ...) that keeps the grid at or under ~4096
-  // work items: enough to fill 256 CUs several times over while each work
-  // item still streams at least 512 keys (256 KiB of K+V).
-  const int64_t pairs = batch * num_kv_heads;
-  int64_t split = 512;
-  while (split < 65536 && pairs * cdiv(max_ctx, split) > 4096) split *= 2;
-  // Never stage more block-table entries than the kernel's LDS holds.
-  while (split > 256 && cdiv(split, page_size) + 1 > kDecodeMaxBt) split /= 2;
-  return int(split);
-}
-
-int make_plan(const Shape& s, int schedule, int decode_split, bool check_pool, Plan* plan,
+int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_pool, Plan* plan,
               std::string* err) {
   if (s.batch < 1 || s.num_q_heads < 1 || s.num_kv_heads < 1 || s.query_len < 1 ||
       s.head_dim < 1 || s.page_size < 1 || s.max_pages < 1)
@@ -69,27 +57,22 @@ int make_plan(const Shape& s, int schedule, int decode_split, bool check_pool, P
     p.rows = int(rows);
     p.rows_pad = 1;
     while (p.rows_pad < p.rows) p.rows_pad *= 2;
-    int split = decode_split;
-    if (split == 0) {
-      split = auto_decode_split(s.batch, s.num_kv_heads, max_ctx, s.page_size);
-    } else if (split < 256 || split > 65536 || split % 256 != 0) {
-      return fail(err, kErrInvalid, "decode_split must be a multiple of 256 in [256, 65536]");
-    }
-    if (cdiv(split, s.page_size) + 1 > kDecodeMaxBt)
-      return fail(err, kErrInvalid, "decode_split / page_size too large for the staged block table");
-    p.split_len = split;
-    p.n_split = int(cdiv(max_ctx, split));
-    p.direct = p.n_split == 1;
-    p.bt_entries = int(cdiv(split, s.page_size) + 1);
-    p.aligned = s.page_size % kDecodeTile == 0;
-    p.num_work = int64_t(p.n_split) * s.num_kv_heads * s.batch;
-    if (p.num_work > INT32_MAX) return fail(err, kErrUnsupported, "decode grid too large");
-    if (!p.direct) {
-      const size_t nrows = size_t(s.batch) * size_t(s.num_q_heads) * size_t(s.query_len);
-      p.ws_acc_offset = 0;
-      p.ws_ml_offset = align_up(nrows * size_t(p.n_split) * kHeadDim * sizeof(float), 256);
-      p.workspace_bytes = align_up(p.ws_ml_offset + nrows * size_t(p.n_split) * 2 * sizeof(float), 256);
-    }
+    if (decode_work_items < 0 || decode_work_items > kDecodeMaxWork)
+      return fail(err, kErrInvalid, "decode_work_items must be in [0, 65536]");
+    p.work_items = decode_work_items;
+    p.work_cap = decode_work_items > 0 ? decode_work_items : kDecodeAutoCap;
+    // granule arithmetic (work item * total granules) must stay inside int64
+    const int64_t granules = s.batch * s.num_kv_heads * cdiv(max_ctx, 64);
+    if (granules > (int64_t(1) << 62) / p.work_cap)
+      return fail(err, kErrUnsupported, "decode work too large for the granule arithmetic");
+    p.bt_entries = int(kDecodeWindow / s.page_size + 2);
+    p.aligned = s.page_size % kDecodeStep == 0;  // a wave step lies inside one page
+    p.num_work = p.work_cap;
+    const size_t slots = size_t(p.work_cap) * 2 * size_t(p.rows);
+    p.ws_pref_offset = 0;
+    p.ws_ml_offset = align_up(size_t(s.batch + 1) * sizeof(int64_t), 256);
+    p.ws_acc_offset = align_up(p.ws_ml_offset + slots * 2 * sizeof(float), 256);
+    p.workspace_bytes = align_up(p.ws_acc_offset + slots * kHeadDim * sizeof(float), 256);
   } else {
     p.n_qtiles = int(cdiv(s.query_len, kPrefillBlockM));
     p.aligned = s.page_size % kPrefillBlockN == 0;

@@ -12,9 +12,11 @@
 namespace pa {
 
 constexpr int kHeadDim = 128;        // the only head_dim the kernels implement
-constexpr int kDecodeTile = 32;      // keys per decode tile (per wave iteration)
+constexpr int kDecodeStep = 16;      // keys per decode wave step
 constexpr int kDecodeMaxRows = 8;    // q rows (GQA group x query_len) per decode work item
-constexpr int kDecodeMaxBt = 2049;   // block-table entries one decode work item stages
+constexpr int kDecodeWindow = 2048;  // keys whose block-table entries a decode work item stages at once
+constexpr int kDecodeAutoCap = 2048; // most decode work items the automatic choice launches
+constexpr int kDecodeMaxWork = 65536;
 constexpr int kPrefillBlockM = 128;  // query rows per prefill work item
 constexpr int kPrefillBlockN = 64;   // keys per prefill K/V tile
 constexpr int kScheduleDecode = 1;
@@ -32,18 +34,18 @@ struct Plan {
   int group = 0;           // num_q_heads / num_kv_heads
   int rows = 0;            // decode: q rows per work item (group * query_len)
   int rows_pad = 0;        // decode: rows rounded up to 1, 2, 4 or 8
-  int split_len = 0;       // decode: keys per split
-  int n_split = 0;         // decode: splits per sequence (upper bound)
-  bool direct = false;     // decode: one split -> write the output directly
-  int bt_entries = 0;      // decode: block-table entries staged per split
+  int work_items = 0;      // decode: requested work items (0 = as many as stay resident)
+  int work_cap = 0;        // decode: most work items the workspace is sized for
+  int bt_entries = 0;      // decode: block-table entries staged per window
   int n_qtiles = 0;        // prefill: query tiles per (sequence, head)
   int ps_log2 = -1;        // log2(page_size) or -1 if not a power of two
   bool aligned = false;    // every tile lies inside one page
   int64_t max_ctx = 0;     // max_pages * page_size
   int64_t num_work = 0;    // work items (workgroups) of the main kernel
   size_t workspace_bytes = 0;
-  size_t ws_acc_offset = 0;  // decode partial accumulators [B*Hq*L][n_split][D] f32
-  size_t ws_ml_offset = 0;   // decode partial (max, sum)   [B*Hq*L][n_split][2] f32
+  size_t ws_pref_offset = 0;  // decode granule prefix [B + 1] int64
+  size_t ws_ml_offset = 0;    // decode partial (max, sum) [work_cap][2][rows][2] f32
+  size_t ws_acc_offset = 0;   // decode partial outputs    [work_cap][2][rows][D] f32
 };
 
 // Error codes (the same values as the PA_ERR_* codes of the C header).
@@ -53,12 +55,9 @@ constexpr int kErrUnsupported = -2;
 constexpr int kErrWorkspace = -3;
 
 // Validates `s` and fills `plan`. `schedule` is 0 (auto), 1 (decode) or
-// 2 (prefill); `decode_split` is 0 (auto) or an explicit split length.
-// Returns kOk or a negative code with a message in `err`.
-int make_plan(const Shape& s, int schedule, int decode_split, bool check_pool, Plan* plan,
+// 2 (prefill); `decode_work_items` is 0 (auto) or an explicit number of
+// decode work items. Returns kOk or a negative code with a message in `err`.
+int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_pool, Plan* plan,
               std::string* err);
-
-// Automatic split length for the decode schedule (exposed for tests).
-int auto_decode_split(int64_t batch, int64_t num_kv_heads, int64_t max_ctx, int64_t page_size);
 
 }  // namespace pa

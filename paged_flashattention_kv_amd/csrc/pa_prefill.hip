@@ -52,6 +52,9 @@ constexpr int kBM = kPrefillBlockM;  // 128 query rows
 constexpr int kBN = kPrefillBlockN;  // 64 keys
 constexpr int kKStride = 128 + 8;    // bf16 per K row in LDS (16 B pad)
 constexpr int kVStride = kBN + 8;    // bf16 per V^T row in LDS (16 B pad)
+// The exponent reference of a row moves only when a tile maximum exceeds it
+// by more than kTau (log2 units), so weights stay <= 2^kTau.
+constexpr float kTau = 8.0f;
 
 struct PrefillArgs {
   const uint16_t* query;
@@ -215,46 +218,55 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
       }
     }
 
-    // ---- scale, mask, online softmax (row = this lane's query row) ----
-    // element i of block kb is key 32kb + 8(i/4) + 4half + i%4 of the tile
+    // ---- mask, online softmax (row = this lane's query row) ----
+    // element i of block kb is key 32kb + 8(i/4) + 4half + i%4 of the tile.
+    // The maximum is taken on raw scores (c > 0); the scale is folded into
+    // the exponent argument.
     const bool need_mask = (t0 + kBN > ctx) || (a.causal && t0 + kBN - 1 > r0 + offset);
-    float tmax = -INFINITY;
+    if (need_mask) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = acc_s[kb][i] * a.c;
-        if (need_mask) {
+        for (int i = 0; i < 16; ++i) {
           const int key = t0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
           const bool vis = key < ctx && (!a.causal || key <= row_abs + offset);
-          x = vis ? x : -INFINITY;
+          acc_s[kb][i] = vis ? acc_s[kb][i] : -INFINITY;
         }
-        acc_s[kb][i] = x;
-        tmax = fmaxf(tmax, x);
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, acc_s[kb][i]);
+    tmax = max_xor32(tmax) * a.c;  // log2 units
+    // The exponent reference moves only when the tile maximum exceeds it by
+    // more than kTau; otherwise the weights stay <= 2^kTau and the output
+    // needs no rescale. The branch is taken when any row of the wave moves.
+    const bool grow = tmax > m_run + kTau;
+    if (__ballot(grow)) {
+      const float alpha = grow ? fast_exp2(m_run - tmax) : 1.f;  // 0 while the old reference is -inf
+      m_run = grow ? tmax : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
+    }
+    const float neg_ref = m_run == -INFINITY ? 0.f : -m_run;
     float psum = 0.f;
     uint32_t pk[2][8];  // P^T operand, packed bf16 pairs
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const float p0 = fast_exp2(acc_s[kb][i] - m_use);
-        const float p1 = fast_exp2(acc_s[kb][i + 1] - m_use);
+        const float p0 = fast_exp2(fmaf(acc_s[kb][i], a.c, neg_ref));
+        const float p1 = fast_exp2(fmaf(acc_s[kb][i + 1], a.c, neg_ref));
         psum += p0 + p1;
         pk[kb][i >> 1] = pack_bf16x2(p0, p1);
       }
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
+    l_run += psum;
 
     // ---- O^T += V^T P^T : 4 blocks of 32 dims, 4 steps of 16 keys ----
 #pragma unroll
@@ -273,7 +285,7 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
 
   // ---- finalize: divide by the row sum, store bf16 ----
   if (!wave_has_rows) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_xor32(l_run);
   if (row_abs >= L) return;
   const float inv = 1.f / l_tot;
   uint16_t* op = a.out + (((size_t)b * a.num_q_heads + head) * L + row_abs) * 128;

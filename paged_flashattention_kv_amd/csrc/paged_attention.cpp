@@ -52,7 +52,7 @@ int paged_attention_ex(const void* query, const void* key_pages, const void* val
                        int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t query_len,
                        int32_t head_dim, int32_t num_pages, int32_t page_size, int32_t max_pages,
                        float scale, int32_t causal, void* workspace, size_t workspace_bytes,
-                       int32_t schedule, int32_t decode_split, void* stream) {
+                       int32_t schedule, int32_t decode_work_items, void* stream) {
   if (!query || !key_pages || !value_pages || !block_table || !context_lens || !out)
     return set_error(PA_ERR_INVALID, "a tensor pointer is NULL");
   if (causal != 0 && causal != 1) return set_error(PA_ERR_INVALID, "causal must be 0 or 1");
@@ -61,7 +61,7 @@ int paged_attention_ex(const void* query, const void* key_pages, const void* val
   std::string err;
   const pa::Shape s = make_shape(batch, num_q_heads, num_kv_heads, query_len, head_dim, num_pages,
                                  page_size, max_pages, causal != 0);
-  const int rc = pa::make_plan(s, schedule, decode_split, true, &plan, &err);
+  const int rc = pa::make_plan(s, schedule, decode_work_items, true, &plan, &err);
   if (rc != pa::kOk) return set_error(rc, err);
   if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
     return set_error(PA_ERR_WORKSPACE, "workspace smaller than paged_attention_workspace_bytes() = " +
@@ -114,12 +114,12 @@ int paged_attention(const void* query, const void* key_pages, const void* value_
 
 size_t paged_attention_workspace_bytes_ex(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                           int32_t query_len, int32_t head_dim, int32_t page_size,
-                                          int32_t max_pages, int32_t schedule, int32_t decode_split) {
+                                          int32_t max_pages, int32_t schedule, int32_t decode_work_items) {
   pa::Plan plan;
   std::string err;
   const pa::Shape s = make_shape(batch, num_q_heads, num_kv_heads, query_len, head_dim, 1, page_size,
                                  max_pages, false);
-  const int rc = pa::make_plan(s, schedule, decode_split, false, &plan, &err);
+  const int rc = pa::make_plan(s, schedule, decode_work_items, false, &plan, &err);
   if (rc != pa::kOk) {
     set_error(rc, err);
     return static_cast<size_t>(-1);

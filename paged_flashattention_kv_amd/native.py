@@ -91,9 +91,9 @@ def _check(code: int) -> None:
 
 
 def workspace_bytes(batch, num_q_heads, num_kv_heads, query_len, head_dim, page_size, max_pages,
-                    schedule=SCHEDULE_AUTO, decode_split=0) -> int:
+                    schedule=SCHEDULE_AUTO, decode_work_items=0) -> int:
     n = load().paged_attention_workspace_bytes_ex(batch, num_q_heads, num_kv_heads, query_len, head_dim,
-                                                  page_size, max_pages, schedule, decode_split)
+                                                  page_size, max_pages, schedule, decode_work_items)
     if n == ctypes.c_size_t(-1).value:
         raise PagedAttentionError(PA_ERR_INVALID, last_error())
     return int(n)
@@ -137,7 +137,7 @@ def paged_attention(
     out: Optional[torch.Tensor] = None,
     workspace: Optional[torch.Tensor] = None,
     schedule: int = SCHEDULE_AUTO,
-    decode_split: int = 0,
+    decode_work_items: int = 0,
     stream: Optional[torch.cuda.Stream] = None,
 ) -> torch.Tensor:
     """Paged attention on the GPU ("Week 3 Day 5: Paged FlashAttention", "Keep the Day 4 Interface").
@@ -173,7 +173,7 @@ def paged_attention(
         _require(out, "out", torch.bfloat16, 4, dev)
         if tuple(out.shape) != tuple(query.shape):
             raise ValueError("out must have the query's shape")
-    need = workspace_bytes(B, Hq, Hkv, L, D, ps, max_pages, schedule, decode_split)
+    need = workspace_bytes(B, Hq, Hkv, L, D, ps, max_pages, schedule, decode_work_items)
     ws_ptr, ws_len = None, 0
     if need > 0:
         if workspace is None:
@@ -185,7 +185,7 @@ def paged_attention(
     rc = lib.paged_attention_ex(
         query.data_ptr(), key_pages.data_ptr(), value_pages.data_ptr(), block_table.data_ptr(),
         context_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, L, D, P, ps, max_pages, float(scale),
-        1 if causal else 0, ws_ptr, ws_len, int(schedule), int(decode_split), _stream_ptr(stream, dev),
+        1 if causal else 0, ws_ptr, ws_len, int(schedule), int(decode_work_items), _stream_ptr(stream, dev),
     )
     _check(rc)
     return out

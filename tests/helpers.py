@@ -32,7 +32,7 @@ def to_device(p, device="cuda:0"):
     )
 
 
-def run_gpu(p, schedule=0, decode_split=0, dev=None, out=None):
+def run_gpu(p, schedule=0, decode_work_items=0, dev=None, out=None):
     """Run the operator on problem ``p``; return float64 numpy [B, H_q, L, D]."""
     import torch
     from paged_flashattention_kv_amd import native
@@ -40,7 +40,7 @@ def run_gpu(p, schedule=0, decode_split=0, dev=None, out=None):
     d = dev if dev is not None else to_device(p)
     o = native.paged_attention(
         d["query"], d["key_pages"], d["value_pages"], d["block_table"], d["context_lens"],
-        p.page_size, p.scale, p.causal, schedule=schedule, decode_split=decode_split, out=out,
+        p.page_size, p.scale, p.causal, schedule=schedule, decode_work_items=decode_work_items, out=out,
     )
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64)

@@ -32,9 +32,9 @@ int main() {
   CHECK(pa::make_plan(shape(1, 32, 8, 100, 128, 16, 4), 0, 0, true, &p, &err) == pa::kErrInvalid);
   CHECK(pa::make_plan(shape(1, 32, 8, 100, 128, 16, 4, false), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(pa::make_plan(shape(1, 32, 8, 1, 128, 16, 4), 3, 0, true, &p, &err) == pa::kErrInvalid);
-  CHECK(pa::make_plan(shape(1, 32, 8, 1, 128, 16, 4), 1, 100, true, &p, &err) == pa::kErrInvalid);
+  CHECK(pa::make_plan(shape(1, 32, 8, 1, 128, 16, 4), 1, -1, true, &p, &err) == pa::kErrInvalid);
+  CHECK(pa::make_plan(shape(1, 32, 8, 1, 128, 16, 4), 1, 65537, true, &p, &err) == pa::kErrInvalid);
   CHECK(pa::make_plan(shape(1, 32, 8, 3, 128, 16, 4), 1, 0, true, &p, &err) == pa::kErrInvalid);
-  CHECK(pa::make_plan(shape(1, 32, 8, 1, 128, 1, 100000), 1, 4096, true, &p, &err) == pa::kErrInvalid);
   CHECK(pa::make_plan(shape(1, 32, 8, 1, 128, 1 << 20, 1 << 12), 0, 0, true, &p, &err) == pa::kErrUnsupported);
   CHECK(!err.empty());
   // dispatch on the query length
@@ -44,10 +44,10 @@ int main() {
       CHECK(p.schedule == (G * L <= 8 ? pa::kScheduleDecode : pa::kSchedulePrefill));
       if (p.schedule == pa::kScheduleDecode) {
         CHECK(p.rows == G * L && p.rows_pad >= p.rows && p.rows_pad <= 8);
-        CHECK(p.split_len % 256 == 0 && p.n_split * (long)p.split_len >= p.max_ctx);
-        CHECK((p.n_split == 1) == p.direct);
-        CHECK(p.direct ? p.workspace_bytes == 0 : p.workspace_bytes >= size_t(3) * 8 * G * L * p.n_split * 130 * 4);
-        CHECK(p.bt_entries <= pa::kDecodeMaxBt);
+        CHECK(p.work_cap == pa::kDecodeAutoCap && p.work_items == 0);
+        CHECK(p.workspace_bytes >= size_t(4) * 8 + size_t(p.work_cap) * 2 * G * L * 130 * 4);
+        CHECK(p.ws_acc_offset % 256 == 0 && p.ws_ml_offset % 256 == 0 && p.ws_ml_offset >= 4 * 8);
+        CHECK(p.bt_entries == pa::kDecodeWindow / 16 + 2);
       } else {
         CHECK(p.n_qtiles == (L + 127) / 128 && p.workspace_bytes == 0);
       }
@@ -57,19 +57,23 @@ int main() {
   CHECK(pa::make_plan(shape(64, 32, 8, 1, 128, 128, 33), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(p.schedule == pa::kScheduleDecode && p.aligned && p.rows == 4);
   CHECK(pa::make_plan(shape(16, 32, 8, 1, 128, 16, 2048), 0, 0, true, &p, &err) == pa::kOk);
-  CHECK(p.schedule == pa::kScheduleDecode && !p.aligned && p.num_work >= 1024);
+  CHECK(p.schedule == pa::kScheduleDecode && p.aligned);
   CHECK(pa::make_plan(shape(4, 32, 8, 2048, 128, 128, 16), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(p.schedule == pa::kSchedulePrefill && p.aligned && p.n_qtiles == 16);
   CHECK(pa::make_plan(shape(8, 32, 8, 65, 128, 128, 30), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(p.schedule == pa::kSchedulePrefill && p.n_qtiles == 1);
   CHECK(pa::make_plan(shape(1, 4, 2, 13, 128, 4, 4), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(p.schedule == pa::kSchedulePrefill && !p.aligned);
-  // automatic split lengths stay within the staged block table
-  for (int ps : {1, 2, 3, 16, 100, 128, 4096})
-    for (int ctx : {1, 100, 5000, 70000, 1 << 20}) {
-      const int s = pa::auto_decode_split(16, 8, ctx, ps);
-      CHECK(s >= 256 && s % 256 == 0 && (s + ps - 1) / ps + 1 <= pa::kDecodeMaxBt);
-    }
+  // a staging window of any page size fits the block-table entries it needs
+  for (int ps : {1, 2, 3, 7, 16, 100, 128, 2047, 2048, 4096}) {
+    CHECK(pa::make_plan(shape(2, 8, 8, 1, 128, ps, 10), 1, 0, true, &p, &err) == pa::kOk);
+    const int worst = (pa::kDecodeWindow - 1 + ps - 1) / ps + 1;  // window starting one key into a page
+    CHECK(p.bt_entries >= worst);
+    CHECK(p.aligned == (ps % pa::kDecodeStep == 0));
+  }
+  // explicit work item counts size the workspace
+  CHECK(pa::make_plan(shape(2, 8, 8, 1, 128, 16, 10), 1, 7, true, &p, &err) == pa::kOk);
+  CHECK(p.work_items == 7 && p.work_cap == 7);
   if (failures == 0) std::printf("plan_check: all passed\n");
   return failures == 0 ? 0 : 1;
 }

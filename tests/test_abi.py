@@ -65,9 +65,11 @@ def _call(lib, **kw):
         (dict(D=64), native.PA_ERR_UNSUPPORTED),
         (dict(sched=7), native.PA_ERR_INVALID),
         (dict(L=5, sched=1), native.PA_ERR_INVALID),  # 10 rows > 8
-        (dict(sched=1, split=300), native.PA_ERR_INVALID),
-        (dict(out=FAKE), native.PA_ERR_INVALID),  # aliases the query
+        (dict(sched=1, split=-1), native.PA_ERR_INVALID),
+        (dict(sched=1, split=70000), native.PA_ERR_INVALID),
+        (dict(out=FAKE, sched=2), native.PA_ERR_INVALID),  # aliases the query
         (dict(mp=400, ps=16, B=2, sched=1, split=256), native.PA_ERR_WORKSPACE),
+        (dict(mp=400, ps=16, B=2), native.PA_ERR_WORKSPACE),
     ],
 )
 def test_invalid_arguments_return_codes(lib, kw, code):
@@ -82,9 +84,10 @@ def test_schedule_rule_and_workspace(lib):
     assert native.schedule_for(1, 8, 8, 8, 128, 128, 33) == native.SCHEDULE_DECODE
     assert native.schedule_for(4, 32, 8, 2048, 128, 128, 16) == native.SCHEDULE_PREFILL
     assert native.workspace_bytes(4, 32, 8, 2048, 128, 128, 16) == 0
-    # long decode: several splits, partials of (D + 2) floats per split and row
+    # decode: granule prefix plus two partial (max, sum, acc[D]) slots per work item and row
     n = native.workspace_bytes(16, 32, 8, 1, 128, 16, 2048)
-    assert n >= 16 * 32 * 2 * 130 * 4
+    assert n >= 17 * 8 + 2048 * 2 * 4 * 130 * 4
+    assert native.workspace_bytes(16, 32, 8, 1, 128, 16, 2048, native.SCHEDULE_DECODE, 100) < n
     with pytest.raises(native.PagedAttentionError):
         native.workspace_bytes(1, 3, 2, 1, 128, 16, 4)
 

@@ -79,13 +79,20 @@ def test_config_decode_batch(decode_batch):
     parity(run_gpu(p), want, "decode_batch auto")
 
 
-@pytest.mark.parametrize("split", [256, 512, 2048, 4096])
-def test_decode_batch_split_lengths(decode_batch, split):
+@pytest.mark.parametrize("items", [1, 7, 100, 513, 4096])
+def test_decode_batch_work_items(decode_batch, items):
     p = decode_batch
-    want = ref(p, pairs=[(b, h) for b in range(0, 64, 5) for h in (0, 13, 31)])
-    got = run_gpu(p, schedule=DECODE, decode_split=split)
-    sel = np.stack([got[b, h] for b in range(0, 64, 5) for h in (0, 13, 31)])
-    parity(sel, want, f"decode_batch split={split}")
+    pairs = [(b, h) for b in range(0, 64, 5) for h in (0, 13, 31)]
+    want = ref(p, pairs=pairs)
+    got = run_gpu(p, schedule=DECODE, decode_work_items=items)
+    parity(np.stack([got[b, h] for b, h in pairs]), want, f"decode_batch items={items}")
+
+
+@pytest.mark.parametrize("items", [1, 3, 64, 5000])
+def test_decode_tiny_contexts_more_items_than_work(items):
+    # contexts of 1..70 keys: a few granules in total, so most work items are empty
+    p = small(44, B=9, Hq=8, Hkv=2, L=1, ctx=(1, 2, 63, 64, 65, 7, 70, 33, 1), ps=16, poison=True)
+    parity(run_gpu(p, schedule=DECODE, decode_work_items=items), ref(p), f"tiny contexts items={items}")
 
 
 def test_config_long_prefill():
@@ -120,6 +127,8 @@ def test_config_long_decode(long_decode):
     want = ref(p, pairs=pairs)
     got = run_gpu(p)
     parity(np.stack([got[b, h] for b, h in pairs]), want, "long_decode")
+    got3 = run_gpu(p, schedule=DECODE, decode_work_items=3)
+    parity(np.stack([got3[b, h] for b, h in pairs]), want, "long_decode items=3")
 
 
 # ------------------------------------------------------- needle probes
