@@ -27,8 +27,9 @@
  *     bf16 is stored as 16-bit words. All index arrays are int32.
  *   - The caller owns every buffer. The library allocates nothing, keeps no
  *     pointer after returning, and has no global state besides the
- *     thread-local error message and a per-device cache of how many decode
- *     work items stay resident. `out` must not alias any input.
+ *     thread-local error message, a per-device cache of how many decode
+ *     work items stay resident, and a call counter that tags each call.
+ *     `out` must not alias any input.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously; results are valid after the stream
  *     is synchronised.
@@ -78,9 +79,13 @@ enum {
  *   causal       0 or 1
  *   workspace    device scratch of at least
  *                paged_attention_workspace_bytes(...) bytes (may be NULL when
- *                that is 0: the prefill schedule needs none); its contents
- *                need no initialisation and are garbage afterwards. Calls
- *                that share a workspace must be ordered on one stream.
+ *                that is 0: the prefill schedule needs none). Zero-fill a
+ *                workspace once before its first use: its head holds the
+ *                decode schedule's arrival counters, which every successful
+ *                call leaves at zero (a counter left by an interrupted call
+ *                carries that call's tag and is ignored). The rest is
+ *                scratch. Calls that share a workspace must be ordered on
+ *                one stream.
  *
  * Device-data preconditions (not checked; see
  * paged_attention_check_metadata): for every b,

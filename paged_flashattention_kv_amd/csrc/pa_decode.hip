@@ -19,7 +19,9 @@
 // A piece that is a whole segment is normalised and stored directly; a
 // piece of a segment shared with other work items (at most the first and
 // the last piece of a range) leaves its (max, sum, acc) state in the
-// workspace, and pa_decode_merge combines those.
+// workspace and counts itself in at the segment's counter; the work item
+// that arrives last combines the segment's partials and stores the output.
+// One kernel launch per call.
 //
 // Inside a piece: all query rows that read this kv head -- the GQA group
 // times the query length, at most 8 rows -- are served by ONE pass over the
@@ -78,9 +80,10 @@ struct DecodeArgs {
   const int32_t* block_table;
   const int32_t* context_lens;
   uint16_t* out;
-  int64_t* ws_pref;  // [batch + 1] granule prefix over sequences (written by work item 0)
+  uint64_t* ws_ctr;  // [batch * num_kv_heads] arrival counters of shared segments (epoch << 32 | count)
   float* ws_ml;      // [work_items][2][rows][2]   partial (reference max, sum)
   float* ws_acc;     // [work_items][2][rows][128] partial unnormalised outputs
+  uint32_t epoch;    // differs from the previous call's and from 0
   int batch, num_q_heads, num_kv_heads, query_len, group, rows;
   int page_size, ps_log2, max_pages;
   int work_items;
@@ -223,6 +226,16 @@ __device__ __forceinline__ void compute_stage(const Stage& st, int t0, int s1, c
     }
   }
 }
+
+// Device-coherent (agent scope, relaxed) accesses of the partial states.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's memory operations (stores included) have completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ int64_t n_gran(int ctx) { return (ctx + kGran - 1) / kGran; }
 
@@ -375,12 +388,86 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
       const size_t orow = ((size_t)b * a.num_q_heads + h) * a.query_len + l;
       a.out[orow * 128 + d] = to_bf16(num / den);
     } else {
-      a.ws_acc[(part + r) * 128 + d] = num;
+      // device-coherent stores (no cache-wide fence needed; see arrive_last)
+      store_coherent(a.ws_acc + (part + r) * 128 + d, num);
       if (d == 0) {
-        a.ws_ml[(part + r) * 2 + 0] = M;
-        a.ws_ml[(part + r) * 2 + 1] = den;
+        store_coherent(a.ws_ml + (part + r) * 2 + 0, M);
+        store_coherent(a.ws_ml + (part + r) * 2 + 1, den);
       }
     }
+  }
+}
+
+// Arrival at a shared segment's counter; true for the last of n arrivals.
+// The counter word holds (epoch << 32 | arrivals so far); a word tagged with
+// another epoch (an earlier call) counts as zero. The last arrival resets
+// the word to 0.
+//
+// Ordering without cache-wide fences (an agent-scope fence writes back and
+// invalidates a whole XCD L2 here): partials are written with device-coherent
+// stores; every wave waits for its stores to complete (vmcnt(0)) before the
+// work item's barrier, and only then is the counter updated. The last
+// arrival reads the partials with device-coherent loads issued after it has
+// seen the final count.
+__device__ __forceinline__ bool arrive_last(uint64_t* ctr, uint32_t epoch, uint32_t n) {
+  uint64_t v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    const uint32_t cnt = (uint32_t)(v >> 32) == epoch ? (uint32_t)v : 0u;
+    const uint64_t nv = cnt + 1 == n ? 0ull : ((uint64_t)epoch << 32 | (cnt + 1));
+    if (__hip_atomic_compare_exchange_strong(ctr, &v, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return cnt + 1 == n;
+  }
+}
+
+// The work items holding pieces of segment [S, E) (granules) and the number
+// of non-empty ones.
+struct SegmentItems {
+  int64_t wf, wl;
+  uint32_t count;
+};
+
+__device__ __forceinline__ SegmentItems segment_items(int64_t S, int64_t E, int64_t total, int64_t P) {
+  SegmentItems it;
+  it.wf = ((S + 1) * P - 1) / total;  // work item holding granule S
+  it.wl = (E * P - 1) / total;        // work item holding granule E - 1
+  it.count = 0;
+  for (int64_t w = it.wf; w <= it.wl; ++w) it.count += gran_begin(w, total, P) < gran_begin(w + 1, total, P);
+  return it;
+}
+
+// Combines the partial states of one shared segment ("Week 2 Day 5", Task 2:
+// common maximum, one rescale factor per partial, one denominator, the head
+// dimensions in parallel). Work item w's piece sits in slot 0 when the
+// segment is the first piece of w's range, else in slot 1. Partials with
+// maximum -inf (no visible key) contribute 0.
+__device__ void merge_segment(const DecodeArgs& a, int b, int kvh, int64_t S, const SegmentItems& it,
+                              int64_t total) {
+  const int64_t P = a.work_items;
+  for (int idx = threadIdx.x; idx < a.rows * 128; idx += kThreads) {
+    const int r = idx >> 7;
+    const int d = idx & 127;
+    float M = -INFINITY;
+    for (int64_t w = it.wf; w <= it.wl; ++w) {
+      const int64_t gw = gran_begin(w, total, P);
+      if (gw == gran_begin(w + 1, total, P)) continue;  // empty work item
+      const size_t part = ((size_t)w * 2 + (gw >= S ? 0 : 1)) * a.rows + r;
+      M = fmaxf(M, load_coherent(a.ws_ml + part * 2));
+    }
+    float den = 0.f, num = 0.f;
+    for (int64_t w = it.wf; w <= it.wl; ++w) {
+      const int64_t gw = gran_begin(w, total, P);
+      if (gw == gran_begin(w + 1, total, P)) continue;
+      const size_t part = ((size_t)w * 2 + (gw >= S ? 0 : 1)) * a.rows + r;
+      const float mj = load_coherent(a.ws_ml + part * 2);
+      const float f = mj == -INFINITY ? 0.f : fast_exp2(mj - M);
+      den = fmaf(f, load_coherent(a.ws_ml + part * 2 + 1), den);
+      num = fmaf(f, load_coherent(a.ws_acc + part * 128 + d), num);
+    }
+    const int h = kvh * a.group + r / a.query_len;
+    const int l = r % a.query_len;
+    const size_t orow = ((size_t)b * a.num_q_heads + h) * a.query_len + l;
+    a.out[orow * 128 + d] = to_bf16(num / den);
   }
 }
 
@@ -392,6 +479,7 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
   __shared__ float lds_acc[kWaves][ROWS][128];
   __shared__ int64_t lds_scan[kThreads];
   __shared__ int64_t lds_start[2];  // (sequence holding the first granule, its granule prefix)
+  __shared__ bool lds_last;
 
   const int tid = threadIdx.x;
   // ---- granule prefix over sequences: thread t sums a contiguous chunk ----
@@ -414,18 +502,16 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
   const int64_t G0 = gran_begin(w, total, a.work_items);
   const int64_t G1 = gran_begin(w + 1, total, a.work_items);
   {
-    // which sequence holds granule G0 (and write the prefix once for the merge)
+    // which sequence holds granule G0
     int64_t pref = excl;
     for (int b = c0; b < c1; ++b) {
       const int64_t ng = n_gran(a.context_lens[b]);
-      if (blockIdx.x == 0) a.ws_pref[b] = pref;
       if (G0 >= pref * a.num_kv_heads && G0 < (pref + ng) * a.num_kv_heads) {
         lds_start[0] = b;
         lds_start[1] = pref;
       }
       pref += ng;
     }
-    if (blockIdx.x == 0 && tid == kThreads - 1) a.ws_pref[a.batch] = total_b;
   }
   __syncthreads();
   if (G0 >= G1) return;  // no work for this item (uniform)
@@ -445,6 +531,15 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
     const int k1 = (int)min((gend - S) * kGran, (int64_t)ctx);
     const bool direct = G == S && gend == E;
     decode_piece<ROWS, ALIGNED>(a, lds_bt, lds_m, lds_l, lds_acc, b, kvh, ctx, k0, k1, direct, nth == 0 ? 0 : 1);
+    if (!direct) {
+      // publish this piece, then the last of the segment's work items merges it
+      wait_stores();
+      __syncthreads();
+      const SegmentItems it = segment_items(S, E, total, a.work_items);
+      if (tid == 0) lds_last = arrive_last(a.ws_ctr + (size_t)b * a.num_kv_heads + kvh, a.epoch, it.count);
+      __syncthreads();
+      if (lds_last) merge_segment(a, b, kvh, S, it, total);
+    }
     G = gend;
     ++nth;
     if (G == base + (int64_t)a.num_kv_heads * ng) {  // past the last kv head of sequence b
@@ -452,51 +547,6 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
       pref += ng;
     }
   }
-}
-
-// Combines the partial states of segments shared by several work items
-// ("Week 2 Day 5", Task 2: common maximum, one rescale factor per partial,
-// one denominator, the head dimensions in parallel). One wave per output
-// row; every lane owns two head dims. The work items covering the row's
-// segment and the slot each used are recomputed from the same even split of
-// the granules. Partials with maximum -inf (no visible key) contribute 0.
-__global__ void __launch_bounds__(64) pa_decode_merge(DecodeArgs a) {
-  const int orow = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int L = a.query_len;
-  const int b = orow / (a.num_q_heads * L);
-  const int h = (orow / L) % a.num_q_heads;
-  const int l = orow % L;
-  const int kvh = h / a.group;
-  const int r = (h - kvh * a.group) * L + l;
-  const int64_t total = a.ws_pref[a.batch] * a.num_kv_heads;
-  const int64_t ng = n_gran(a.context_lens[b]);
-  const int64_t S = a.ws_pref[b] * a.num_kv_heads + kvh * ng, E = S + ng;
-  const int64_t P = a.work_items;
-  const int64_t wf = ((S + 1) * P - 1) / total;  // work item holding granule S
-  const int64_t wl = (E * P - 1) / total;        // work item holding granule E - 1
-  if (wf == wl) return;                          // whole segment in one item: stored directly
-  float M = -INFINITY;
-  for (int64_t w = wf; w <= wl; ++w) {
-    const int64_t gw = gran_begin(w, total, P);
-    if (gw == gran_begin(w + 1, total, P)) continue;  // empty work item
-    const size_t part = ((size_t)w * 2 + (gw >= S ? 0 : 1)) * a.rows + r;
-    M = fmaxf(M, a.ws_ml[part * 2]);
-  }
-  float den = 0.f, n0 = 0.f, n1 = 0.f;
-  for (int64_t w = wf; w <= wl; ++w) {
-    const int64_t gw = gran_begin(w, total, P);
-    if (gw == gran_begin(w + 1, total, P)) continue;
-    const size_t part = ((size_t)w * 2 + (gw >= S ? 0 : 1)) * a.rows + r;
-    const float mj = a.ws_ml[part * 2];
-    const float f = mj == -INFINITY ? 0.f : fast_exp2(mj - M);
-    const f32x2_t v = *reinterpret_cast<const f32x2_t*>(a.ws_acc + part * 128 + 2 * lane);
-    den = fmaf(f, a.ws_ml[part * 2 + 1], den);
-    n0 = fmaf(f, v.x, n0);
-    n1 = fmaf(f, v.y, n1);
-  }
-  const float inv = 1.f / den;
-  *reinterpret_cast<uint32_t*>(a.out + (size_t)orow * 128 + 2 * lane) = pack_bf16x2(n0 * inv, n1 * inv);
 }
 
 template <int ROWS, bool ALIGNED>
@@ -544,7 +594,7 @@ hipError_t launch_decode(const KernelArgs& k, const Plan& p, hipStream_t stream)
   a.context_lens = k.context_lens;
   a.out = static_cast<uint16_t*>(k.out);
   char* ws = static_cast<char*>(k.workspace);
-  a.ws_pref = reinterpret_cast<int64_t*>(ws + p.ws_pref_offset);
+  a.ws_ctr = reinterpret_cast<uint64_t*>(ws + p.ws_ctr_offset);
   a.ws_ml = reinterpret_cast<float*>(ws + p.ws_ml_offset);
   a.ws_acc = reinterpret_cast<float*>(ws + p.ws_acc_offset);
   a.batch = k.batch;
@@ -558,6 +608,7 @@ hipError_t launch_decode(const KernelArgs& k, const Plan& p, hipStream_t stream)
   a.max_pages = k.max_pages;
   a.c = k.scale * kLog2e;
   a.causal = k.causal;
+  a.epoch = k.epoch;
   const size_t lds = (size_t)p.bt_entries * sizeof(int32_t);
   hipError_t e;
   switch (p.rows_pad) {
@@ -566,10 +617,7 @@ hipError_t launch_decode(const KernelArgs& k, const Plan& p, hipStream_t stream)
     case 4: e = launch_rows<4>(a, p.aligned, p.work_items, p.work_cap, lds, stream); break;
     default: e = launch_rows<8>(a, p.aligned, p.work_items, p.work_cap, lds, stream); break;
   }
-  if (e != hipSuccess) return e;
-  const int64_t nrows = (int64_t)k.batch * k.num_q_heads * k.query_len;
-  hipLaunchKernelGGL(pa_decode_merge, dim3((unsigned)nrows), dim3(64), 0, stream, a);
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace pa

@@ -20,6 +20,7 @@ struct KernelArgs {
   int batch, num_q_heads, num_kv_heads, query_len, num_pages, page_size, max_pages;
   float scale;
   int causal;
+  uint32_t epoch;  // per-call tag of the decode arrival counters (never 0)
 };
 
 // Short-query split-context schedule (pa_decode.hip).

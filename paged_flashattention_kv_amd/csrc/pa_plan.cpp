@@ -69,8 +69,8 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
     p.aligned = s.page_size % kDecodeStep == 0;  // a wave step lies inside one page
     p.num_work = p.work_cap;
     const size_t slots = size_t(p.work_cap) * 2 * size_t(p.rows);
-    p.ws_pref_offset = 0;
-    p.ws_ml_offset = align_up(size_t(s.batch + 1) * sizeof(int64_t), 256);
+    p.ws_ctr_offset = 0;
+    p.ws_ml_offset = align_up(size_t(s.batch) * size_t(s.num_kv_heads) * sizeof(uint64_t), 256);
     p.ws_acc_offset = align_up(p.ws_ml_offset + slots * 2 * sizeof(float), 256);
     p.workspace_bytes = align_up(p.ws_acc_offset + slots * kHeadDim * sizeof(float), 256);
   } else {

@@ -43,7 +43,7 @@ struct Plan {
   int64_t max_ctx = 0;     // max_pages * page_size
   int64_t num_work = 0;    // work items (workgroups) of the main kernel
   size_t workspace_bytes = 0;
-  size_t ws_pref_offset = 0;  // decode granule prefix [B + 1] int64
+  size_t ws_ctr_offset = 0;   // decode arrival counters [B * H_kv] u64 (zero-filled before first use)
   size_t ws_ml_offset = 0;    // decode partial (max, sum) [work_cap][2][rows][2] f32
   size_t ws_acc_offset = 0;   // decode partial outputs    [work_cap][2][rows][D] f32
 };

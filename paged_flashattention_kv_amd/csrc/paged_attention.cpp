@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <string>
@@ -16,6 +17,13 @@
 namespace {
 
 thread_local std::string g_last_error;
+std::atomic<uint32_t> g_epoch{0};
+
+uint32_t next_epoch() {
+  uint32_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  while (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  return e;
+}
 
 int set_error(int code, const std::string& msg) {
   g_last_error = msg;
@@ -92,6 +100,7 @@ int paged_attention_ex(const void* query, const void* key_pages, const void* val
   k.max_pages = max_pages;
   k.scale = scale;
   k.causal = causal;
+  k.epoch = next_epoch();
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = plan.schedule == pa::kScheduleDecode ? pa::launch_decode(k, plan, st)
                                                             : pa::launch_prefill(k, plan, st);

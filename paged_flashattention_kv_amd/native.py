@@ -145,8 +145,11 @@ def paged_attention(
     query [B, H_q, L, D] bf16; key_pages / value_pages [num_pages, H_kv,
     page_size, D] bf16; block_table [B, max_pages] int32; context_lens [B]
     int32 -- all on one GPU. ``scale`` defaults to 1/sqrt(D). Returns
-    ``out`` [B, H_q, L, D] bf16 (allocated when not given). The call is
-    asynchronous on ``stream`` (default: the current stream).
+    ``out`` [B, H_q, L, D] bf16 (allocated when not given). A caller-owned
+    ``workspace`` (uint8, at least ``workspace_bytes(...)``) must be
+    zero-filled before its first use and can then be reused across calls on
+    one stream. The call is asynchronous on ``stream`` (default: the current
+    stream).
     """
     dev = query.device
     if dev.type != "cuda":
@@ -177,7 +180,7 @@ def paged_attention(
     ws_ptr, ws_len = None, 0
     if need > 0:
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
         if workspace.device != dev or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on the query's device")
         ws_ptr, ws_len = workspace.data_ptr(), workspace.numel() * workspace.element_size()

@@ -45,8 +45,9 @@ int main() {
       if (p.schedule == pa::kScheduleDecode) {
         CHECK(p.rows == G * L && p.rows_pad >= p.rows && p.rows_pad <= 8);
         CHECK(p.work_cap == pa::kDecodeAutoCap && p.work_items == 0);
-        CHECK(p.workspace_bytes >= size_t(4) * 8 + size_t(p.work_cap) * 2 * G * L * 130 * 4);
-        CHECK(p.ws_acc_offset % 256 == 0 && p.ws_ml_offset % 256 == 0 && p.ws_ml_offset >= 4 * 8);
+        CHECK(p.workspace_bytes >= size_t(3) * 8 * 8 + size_t(p.work_cap) * 2 * G * L * 130 * 4);
+        CHECK(p.ws_acc_offset % 256 == 0 && p.ws_ml_offset % 256 == 0 && p.ws_ml_offset >= 3 * 8 * 8);
+        CHECK(p.ws_ctr_offset == 0);
         CHECK(p.bt_entries == pa::kDecodeWindow / 16 + 2);
       } else {
         CHECK(p.n_qtiles == (L + 127) / 128 && p.workspace_bytes == 0);

@@ -84,9 +84,9 @@ def test_schedule_rule_and_workspace(lib):
     assert native.schedule_for(1, 8, 8, 8, 128, 128, 33) == native.SCHEDULE_DECODE
     assert native.schedule_for(4, 32, 8, 2048, 128, 128, 16) == native.SCHEDULE_PREFILL
     assert native.workspace_bytes(4, 32, 8, 2048, 128, 128, 16) == 0
-    # decode: granule prefix plus two partial (max, sum, acc[D]) slots per work item and row
+    # decode: arrival counters plus two partial (max, sum, acc[D]) slots per work item and row
     n = native.workspace_bytes(16, 32, 8, 1, 128, 16, 2048)
-    assert n >= 17 * 8 + 2048 * 2 * 4 * 130 * 4
+    assert n >= 16 * 8 * 8 + 2048 * 2 * 4 * 130 * 4
     assert native.workspace_bytes(16, 32, 8, 1, 128, 16, 2048, native.SCHEDULE_DECODE, 100) < n
     with pytest.raises(native.PagedAttentionError):
         native.workspace_bytes(1, 3, 2, 1, 128, 16, 4)

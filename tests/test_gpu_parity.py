@@ -333,3 +333,28 @@ def test_metadata_check():
     badt[0, 1] = p.num_pages
     with pytest.raises(native.PagedAttentionError):
         native.check_metadata(badt, d["context_lens"], p.num_pages, p.page_size, 4)
+
+
+def test_decode_workspace_reuse_and_stale_counters():
+    import torch
+    from paged_flashattention_kv_amd import native
+
+    p = small(83, B=6, Hq=8, Hkv=2, L=1, ctx=(900, 3000, 70, 1500, 2222, 64), ps=32, poison=True)
+    want = ref(p)
+    d = to_device(p)
+    need = native.workspace_bytes(p.batch, 8, 2, 1, 128, p.page_size, p.max_pages, DECODE, 37)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    ctr = ws[: p.batch * 2 * 8].view(torch.int64)
+    for call in range(4):
+        if call == 2:
+            ctr.fill_(-(1 << 32) + 5)  # left by an interrupted call: another tag, count 5
+        out = native.paged_attention(d["query"], d["key_pages"], d["value_pages"], d["block_table"],
+                                     d["context_lens"], p.page_size, p.scale, True, workspace=ws,
+                                     schedule=DECODE, decode_work_items=37)
+        torch.cuda.synchronize()
+        parity(out.float().cpu().numpy().astype(np.float64), want, f"workspace reuse call {call}")
+        if call < 2:
+            assert (ctr == 0).all(), "a clean workspace must be left at zero"
+        else:
+            # shared segments reset their counter; the others keep the stale tag, which is ignored
+            assert ((ctr == 0) | (ctr == -(1 << 32) + 5)).all()
