@@ -1,0 +1,288 @@
+"""Benchmark of the paged attention operator on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+
+A step is one call of the operator (one kernel launch of the schedule the
+dispatcher picks) over one batch of synthetic input. The headline workload
+is the decode batch at the Qwen3-4B attention shape (B=64, H_q=32, H_kv=8,
+D=128, L=1, context lengths U[128, 4096] not tile multiples, 128-token
+pages shuffled over a pool sized to what the batch needs). Inputs are
+resident in HBM before the timed region. Three independent copies of the
+K/V page pool are rotated step by step so that the 256 MB Infinity Cache
+cannot serve repeated reads.
+
+Printed: one JSON line. ``value`` is decode K/V throughput in TB/s
+(algorithmic bytes: 4096 B per visible context position = H_kv * D * 2
+bytes * (K + V)). ``roofline`` compares the kernel against the 8 TB/s HBM
+peak; its ``traffic`` field is the HBM byte count measured with rocprofv3
+counters for this kernel source (null when the source changed since).
+``cpu_baseline`` is the float64 CPU oracle timed on this host's cores over
+whole passes of the same workload. ``extra`` holds the long causal prefill
+(TFLOP/s against the dense bf16 MFMA peak) and the long-context decode.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode K/V TB/s (% HBM peak); causal prefill TFLOP/s (% bf16 MFMA peak)"
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+POOL_COPIES = 3
+KERNEL_SOURCES = {
+    "pa_decode_work": ["paged_flashattention_kv_amd/csrc/pa_decode.hip", "paged_flashattention_kv_amd/csrc/pa_device.h"],
+    "pa_prefill_mfma": ["paged_flashattention_kv_amd/csrc/pa_prefill.hip", "paged_flashattention_kv_amd/csrc/pa_device.h"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if still current.
+
+    profiles/<kernel>__<workload>.md ends with a line
+    ``traffic_bytes_per_launch: N source_sha: H``; the count is used only
+    while the kernel's source still hashes to H.
+    """
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}.md")
+    try:
+        with open(path) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch: (\d+) source_sha: ([0-9a-f]+)", text)
+    if not m or m.group(2) != source_hash(kernel):
+        return None
+    return int(m.group(1))
+
+
+class Case:
+    """Device copies of a problem plus a callable that runs one step."""
+
+    def __init__(self, p, copies: int):
+        import torch
+        from paged_flashattention_kv_amd import native
+        from paged_flashattention_kv_amd.workloads import PagedProblem  # noqa: F401
+
+        self.p = p
+        dev = "cuda:0"
+
+        def bf(a):
+            import numpy as np
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.q = bf(p.query)
+        k = bf(p.key_pages)
+        v = bf(p.value_pages)
+        self.pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(copies - 1)]
+        self.bt = torch.from_numpy(p.block_table).to(dev)
+        self.ctx = torch.from_numpy(p.context_lens).to(dev)
+        self.out = torch.empty_like(self.q)
+        need = native.workspace_bytes(p.batch, p.num_q_heads, p.num_kv_heads, p.query_len, p.head_dim,
+                                      p.page_size, p.max_pages)
+        self.ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+        self.schedule = native.schedule_for(p.batch, p.num_q_heads, p.num_kv_heads, p.query_len, p.head_dim,
+                                            p.page_size, p.max_pages)
+        self.i = 0
+        self._native = native
+
+    def step(self):
+        k, v = self.pools[self.i % len(self.pools)]
+        self.i += 1
+        self._native.paged_attention(self.q, k, v, self.bt, self.ctx, self.p.page_size, self.p.scale, self.p.causal,
+                                     out=self.out, workspace=self.ws)
+
+    def time(self, steps: int, warmup: int):
+        """ms per step over exactly ``steps`` calls, HIP events on the launch stream."""
+        import torch
+
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(steps):
+            self.step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return start.elapsed_time(stop) / steps, wall / steps * 1e3
+
+
+def cpu_baseline(p, min_seconds: float):
+    """float64 oracle on whole passes over the workload; TB/s over the same algorithmic bytes."""
+    import oracle
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"), default=None)
+    except Exception:
+        threads = None
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.paged_attention_ref(p.query, p.key_pages, p.value_pages, p.block_table, p.context_lens,
+                                   p.page_size, p.scale, p.causal)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {
+        "value": round(p.kv_bytes() * passes / el / 1e12, 6),
+        "unit": "TB/s",
+        "cores": int(threads or os.cpu_count() or 1),
+        "kind": "oracle",
+        "sample": f"{passes} full passes over the {p.name} workload ({p.batch} sequences, "
+                  f"{int(p.context_lens.sum())} context positions) in {el:.1f} s; float64 NumPy/BLAS, "
+                  f"host has {os.cpu_count()} logical CPUs",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one 1 GiB device copy (reference for counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this operator build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_flashattention_kv_amd import native, workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    native.load()
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # ---- headline: decode batch ----
+    p = wl.make_config("decode_batch")
+    case = Case(p, POOL_COPIES)
+    ms, wall_ms = case.time(args.steps, args.warmup)
+    kv = p.kv_bytes()
+    tbps = kv / (ms * 1e-3) / 1e12
+    achieved_gbps = kv / (ms * 1e-3) / 1e9
+    traffic = measured_traffic("pa_decode_work", "decode_batch")
+    result = {
+        "metric": METRIC,
+        "value": round(tbps, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_batch: B=64 L=1 H_q=32 H_kv=8 D=128, context U[128,4096] (seed 2), "
+                        "page_size=128, shuffled pool",
+            "batch": p.batch, "query_len": 1, "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+            "page_size": p.page_size, "context_positions": int(p.context_lens.sum()),
+            "kv_bytes_per_step": kv, "pool_copies_rotated": POOL_COPIES, "schedule": "decode",
+            "wall_ms_per_step": round(wall_ms, 5),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "pa_decode_work",
+            "algorithmic_bytes_per_launch": kv,
+        },
+    }
+    del case
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        extra = {}
+        pp = wl.make_config("long_prefill")
+        c3 = Case(pp, 1)
+        ms3, _ = c3.time(max(20, args.steps // 4), max(5, args.warmup // 4))
+        tf = pp.flops() / (ms3 * 1e-3) / 1e12
+        extra["long_prefill"] = {
+            "workload": "B=4 L=ctx=2048 H_q=32 H_kv=8 D=128 causal, page_size=128 shuffled",
+            "ms_per_step": round(ms3, 5), "value": round(tf, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("pa_prefill_mfma", "long_prefill"),
+                         "kernel": "pa_prefill_mfma", "algorithmic_flops_per_launch": pp.flops()},
+        }
+        del c3
+        torch.cuda.empty_cache()
+        pc = wl.make_config("chunked_continuation")
+        c4 = Case(pc, POOL_COPIES)
+        ms4, _ = c4.time(max(20, args.steps // 4), max(5, args.warmup // 4))
+        extra["chunked_continuation"] = {
+            "workload": "B=8 L=65 history U[1000,3600] (seed 4) H_q=32 H_kv=8 D=128 causal, page_size=128",
+            "ms_per_step": round(ms4, 5),
+            "tflops": round(pc.flops() / (ms4 * 1e-3) / 1e12, 2),
+            "kv_tbps": round(pc.kv_bytes() / (ms4 * 1e-3) / 1e12, 4),
+        }
+        del c4
+        torch.cuda.empty_cache()
+        pl = wl.make_config("long_decode")
+        c5 = Case(pl, 1)  # 2 GiB per step already exceeds the Infinity Cache
+        ms5, _ = c5.time(max(10, args.steps // 10), max(3, args.warmup // 10))
+        g5 = pl.kv_bytes() / (ms5 * 1e-3) / 1e9
+        extra["long_decode"] = {
+            "workload": "B=16 L=1 ctx=32768 H_q=32 H_kv=8 D=128, page_size=16 shuffled over 32768 pages",
+            "ms_per_step": round(ms5, 5), "value": round(g5 / 1e3, 4), "unit": "TB/s",
+            "roofline": {"bound": "hbm", "achieved": round(g5, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(g5 / HBM_PEAK_GBPS, 4),
+                         "traffic": measured_traffic("pa_decode_work", "long_decode"),
+                         "kernel": "pa_decode_work", "algorithmic_bytes_per_launch": pl.kv_bytes()},
+        }
+        del c5
+        torch.cuda.empty_cache()
+        result["extra"] = extra
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
