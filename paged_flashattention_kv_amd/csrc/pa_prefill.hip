@@ -19,22 +19,26 @@
 //   ONE query row (l % 32): the row maximum needs a single cross-lane
 //   exchange (lane l ^ 32), and the rescale factor of a row lives in the
 //   lane that owns that row of the output.
-//   Output O^T = V^T P^T (A = V^T from LDS, B = P^T straight from the score
+//   Output O^T = V^T P^T (A = V^T, B = P^T straight from the score
 //   registers converted to bf16): the 8 keys a lane feeds to one MFMA are
 //   exactly the 8 scores it already holds, so P never goes through LDS.
-//   V is stored transposed in LDS with the keys of every 16-key step
-//   permuted (bits 2 and 3 of the key index swapped) so each lane's 8 keys
-//   are one 16-byte LDS read.
+//   V stays in its natural [key][dim] layout in LDS; the transposed operand
+//   comes from ds_read_b64_tr_b16, which hands lane i of each 16-lane group
+//   element (i mod 4) of the 8 bytes addressed by lane 4j + i/4 as its
+//   element j.
 //
 // Page-translating loader ("Week 3 Day 5", Task 1): each K/V tile is
-// resolved through block_table while it is staged: thread t loads head dims
-// [8(t%16), 8(t%16)+8) of keys 4(t/16) .. 4(t/16)+3 (16 lanes cover a
-// 256-byte row, so a wave reads 4 full rows per instruction). Aligned path
+// resolved through block_table while it is staged, straight from HBM into
+// LDS (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l). A
+// wave instruction moves 4 key rows of 256 bytes. Rows are stored with their
+// 16-byte chunks XOR-swizzled by the key index so that both the K fragment
+// reads and the V transposed reads spread over all LDS banks. Aligned path
 // (page_size % 64 == 0): the tile is one contiguous span of one page, found
 // with a single table entry. Generic path: each key row is translated on
-// its own (tiles that cross pages). Keys at or past the context end are not
-// loaded (zero) and their scores are masked to -inf separately. The next
-// tile is fetched into registers while the current one is computed.
+// its own (tiles that cross pages). Keys at or past the context end read a
+// valid row instead of their (possibly missing) page; their scores are
+// masked to -inf separately. Two LDS buffers: tile t+1 streams in while tile
+// t is computed, one barrier per tile.
 //
 // Work items are ordered so that the heaviest causal query tiles start
 // first and the query heads that share one K/V head run back to back on
@@ -48,13 +52,16 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBM = kPrefillBlockM;  // 128 query rows
-constexpr int kBN = kPrefillBlockN;  // 64 keys
-constexpr int kKStride = 128 + 8;    // bf16 per K row in LDS (16 B pad)
-constexpr int kVStride = kBN + 8;    // bf16 per V^T row in LDS (16 B pad)
+constexpr int kBM = kPrefillBlockM;       // 128 query rows
+constexpr int kBN = kPrefillBlockN;       // 64 keys
+constexpr int kTileBytes = kBN * 256;     // one K (or V) tile in LDS: 16 KiB
 // The exponent reference of a row moves only when a tile maximum exceeds it
 // by more than kTau (log2 units), so weights stay <= 2^kTau.
 constexpr float kTau = 8.0f;
+
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 struct PrefillArgs {
   const uint16_t* query;
@@ -71,69 +78,75 @@ struct PrefillArgs {
 
 __device__ __forceinline__ int div_ps(int s, int ps, int ps_log2) { return ps_log2 >= 0 ? (s >> ps_log2) : s / ps; }
 
-// Position of key k (0..63) inside a V^T row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+// 16-byte chunk c of key row `key` sits at chunk position c ^ swz(key).
+__device__ __forceinline__ int swz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
+
+// Byte offset of (key, chunk) inside a tile buffer.
+__device__ __forceinline__ int tile_off(int key, int chunk) { return key * 256 + ((chunk ^ swz(key)) << 4); }
+
+// Page lookup for the next tile to stage: the element offset of the key row
+// each of the lane's 4 load instructions reads (generic path), or the
+// tile's base row (aligned path, one entry).
+template <bool ALIGNED>
+struct TilePages {
+  size_t row[ALIGNED ? 1 : 4];
+};
+
+typedef __attribute__((address_space(4))) const int32_t constant_i32;
 
 template <bool ALIGNED>
-__device__ __forceinline__ void load_kv_tile(const PrefillArgs& a, int b, int kvh, int ctx, int t0, int tid,
-                                             u32x4_t kreg[4], u32x4_t vreg[4]) {
-  const int dchunk = tid & 15;
-  const int g4 = tid >> 4;
-  const size_t head_stride = (size_t)a.page_size * 128;
-  const size_t page_stride = head_stride * a.num_kv_heads;
-  const size_t head_off = (size_t)kvh * head_stride;
-  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
-  size_t base = 0;
+__device__ __forceinline__ void lookup_tile(const PrefillArgs& a, const int32_t* bt_row, size_t page_stride,
+                                            size_t head_off, int ctx, int t0, int wave, int lane,
+                                            TilePages<ALIGNED>& tp) {
   if (ALIGNED) {
+    // one uniform entry per tile: a scalar load (the table is read-only here)
     const int lp = div_ps(t0, a.page_size, a.ps_log2);
-    const int slot0 = t0 - lp * a.page_size;
-    base = (size_t)bt_row[lp] * page_stride + head_off + (size_t)slot0 * 128;
-  }
+    const int32_t page = ((constant_i32*)bt_row)[lp];
+    tp.row[0] = (size_t)page * page_stride + head_off + (size_t)(t0 - lp * a.page_size) * 128;
+  } else {
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int key = t0 + 4 * g4 + jj;
-    if (key < ctx) {
-      size_t off;
-      if (ALIGNED) {
-        off = base + (size_t)(4 * g4 + jj) * 128;
-      } else {
-        const int lp = div_ps(key, a.page_size, a.ps_log2);
-        const int slot = key - lp * a.page_size;
-        off = (size_t)bt_row[lp] * page_stride + head_off + (size_t)slot * 128;
-      }
-      kreg[jj] = *reinterpret_cast<const u32x4_t*>(a.kpages + off + dchunk * 8);
-      vreg[jj] = *reinterpret_cast<const u32x4_t*>(a.vpages + off + dchunk * 8);
-    } else {
-      kreg[jj] = u32x4_t{0u, 0u, 0u, 0u};
-      vreg[jj] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 4; ++i) {
+      int key = t0 + 4 * (4 * wave + i) + (lane >> 4);
+      key = key < ctx ? key : ctx - 1;  // past the context: re-read a valid row
+      const int lp = div_ps(key, a.page_size, a.ps_log2);
+      tp.row[i] = (size_t)bt_row[lp] * page_stride + head_off + (size_t)(key - lp * a.page_size) * 128;
     }
   }
 }
 
-__device__ __forceinline__ void store_kv_tile(uint16_t* lds_k, uint16_t* lds_vt, int tid, const u32x4_t kreg[4],
-                                              const u32x4_t vreg[4]) {
-  const int dchunk = tid & 15;
-  const int g4 = tid >> 4;
+// Issues the direct HBM -> LDS loads of one K/V tile. Wave w moves keys
+// [16w, 16w + 16) of the tile: instruction i covers keys 4(4w+i) .. +3, lane
+// l key 4(4w+i) + l/16 and LDS chunk position l % 16, which holds global
+// chunk (l % 16) ^ swz(key).
+template <bool ALIGNED>
+__device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages<ALIGNED>& tp, int ctx, int t0,
+                                           int wave, int lane, char* kbuf, char* vbuf) {
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj)
-    *reinterpret_cast<u32x4_t*>(lds_k + (4 * g4 + jj) * kKStride + dchunk * 8) = kreg[jj];
-  // V^T: dim 8*dchunk + e of keys 4*g4 .. 4*g4+3 -> 4 adjacent positions.
-  const int pos = vt_pos(4 * g4);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t w0 = vreg[0][e], w1 = vreg[1][e], w2 = vreg[2][e], w3 = vreg[3][e];
-    // even dim 2e: low halves; odd dim 2e+1: high halves
-    const u32x2_t even = {__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u)};
-    const u32x2_t odd = {__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u)};
-    *reinterpret_cast<u32x2_t*>(lds_vt + (dchunk * 8 + 2 * e) * kVStride + pos) = even;
-    *reinterpret_cast<u32x2_t*>(lds_vt + (dchunk * 8 + 2 * e + 1) * kVStride + pos) = odd;
+  for (int i = 0; i < 4; ++i) {
+    const int key = 4 * (4 * wave + i) + (lane >> 4);  // key inside the tile
+    const int chunk = (lane & 15) ^ swz(key);
+    size_t row;
+    if (ALIGNED) {
+      // the tile lies in one page; keys past the context re-read the tile's first row
+      row = tp.row[0] + (size_t)(t0 + key < ctx ? key : 0) * 128;
+    } else {
+      row = tp.row[i];
+    }
+    const size_t off = row + (size_t)chunk * 8;
+    const int lds_off = (4 * wave + i) * 1024;
+    __builtin_amdgcn_global_load_lds((global_void*)(a.kpages + off), (lds_void*)(kbuf + lds_off), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_void*)(a.vpages + off), (lds_void*)(vbuf + lds_off), 16, 0, 0);
   }
 }
 
+__device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <bool ALIGNED>
 __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kBN * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_vt[128 * kVStride];
+  __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[kTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -171,11 +184,24 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
   const int wave_last_row = min(r0 + 31, L - 1);
   const int wave_kv_end = a.causal ? min(ctx, wave_last_row + offset + 1) : ctx;
 
+  const size_t head_stride = (size_t)a.page_size * 128;
+  const size_t page_stride = head_stride * a.num_kv_heads;
+  const size_t head_off = (size_t)kvh * head_stride;
+  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
+
+  // ---- first tile in flight before anything else ----
+  TilePages<ALIGNED> tp;
+  if (n_tiles > 0) {
+    lookup_tile<ALIGNED>(a, bt_row, page_stride, head_off, ctx, 0, wave, lane, tp);
+    issue_tile<ALIGNED>(a, tp, ctx, 0, wave, lane, lds_k0, lds_v0);
+    lookup_tile<ALIGNED>(a, bt_row, page_stride, head_off, ctx, min(1, n_tiles - 1) * kBN, wave, lane, tp);
+  }
+
   // ---- Q^T operand: lane holds row r0 + col, dims 16ks + 8half .. +8 ----
   bf16x8_t qv[8];
   {
     const int row = r0 + col;
-    const uint16_t* qp = a.query + (((size_t)b * a.num_q_heads + head) * L + row) * 128 + 8 * half;
+    const uint16_t* qp = a.query + (((size_t)b * a.num_q_heads + head) * L + (row < L ? row : 0)) * 128 + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       u32x4_t w = u32x4_t{0u, 0u, 0u, 0u};
@@ -192,96 +218,126 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
   float m_run = -INFINITY;
   float l_run = 0.f;  // this lane's half of the row sum
 
-  u32x4_t kreg[4], vreg[4];
-  if (n_tiles > 0) load_kv_tile<ALIGNED>(a, b, kvh, ctx, 0, tid, kreg, vreg);
+  // LDS reads of this lane (tile-relative):
+  // K fragment (kb, ks): key 32kb + col, chunk 2ks + half.
+  // V^T fragment (db, ks): keys 16ks + 4half + (lane%16)/4 and that + 8,
+  //   dims 32db + 16((lane/16)&1) + 4(lane%4) .. +4, i.e. chunk
+  //   4db + 2((lane/16)&1) + (lane%4)/2 at byte 8(lane&1) inside it.
+  const int vk_lane = 4 * half + ((lane & 15) >> 2);
+  const int vc_lane = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vb_lane = 8 * (lane & 1);
+  const uint32_t ones_bf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
   const int row_abs = r0 + col;
-  for (int t = 0; t < n_tiles; ++t) {
+  // One tile: wait for its loads, barrier, start the next tile's loads into
+  // the other buffer, compute. The buffers are distinct LDS objects chosen
+  // statically (the loop is unrolled by two), so no wait is needed between
+  // the next tile's loads and this tile's reads.
+  auto tile_step = [&](int t, const char* kb_base, const char* vb_base, char* knext, char* vnext) {
     const int t0 = t * kBN;
-    __syncthreads();  // every wave is done reading the previous tile
-    store_kv_tile(lds_k, lds_vt, tid, kreg, vreg);
-    __syncthreads();
-    if (t + 1 < n_tiles) load_kv_tile<ALIGNED>(a, b, kvh, ctx, t0 + kBN, tid, kreg, vreg);
-    if (!wave_has_rows || t0 >= wave_kv_end) continue;
+    wait_all_loads();  // this wave's part of tile t (and the next lookup) has landed
+    __syncthreads();   // every wave's part is in LDS; every wave is done with tile t - 1
+    if (t + 1 < n_tiles) issue_tile<ALIGNED>(a, tp, ctx, t0 + kBN, wave, lane, knext, vnext);
+    // lookup for tile t + 2 (clamped so that it is unconditional)
+    lookup_tile<ALIGNED>(a, bt_row, page_stride, head_off, ctx, min(t + 2, n_tiles - 1) * kBN, wave, lane, tp);
+    if (!wave_has_rows || t0 >= wave_kv_end) return;
 
-    // ---- S^T = K Q^T : two 32-key blocks ----
-    f32x16_t acc_s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc_s[kb][i] = 0.f;
-      const uint16_t* kp = lds_k + (32 * kb + col) * kKStride + 8 * half;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8_t kfrag = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(kp + 16 * ks));
-        acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qv[ks], acc_s[kb], 0, 0, 0);
-      }
-    }
-
-    // ---- mask, online softmax (row = this lane's query row) ----
-    // element i of block kb is key 32kb + 8(i/4) + 4half + i%4 of the tile.
-    // The maximum is taken on raw scores (c > 0); the scale is folded into
-    // the exponent argument.
-    const bool need_mask = (t0 + kBN > ctx) || (a.causal && t0 + kBN - 1 > r0 + offset);
-    if (need_mask) {
-#pragma unroll
+      // ---- S^T = K Q^T : two 32-key blocks ----
+      f32x16_t acc_s[2];
+  #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = t0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-          const bool vis = key < ctx && (!a.causal || key <= row_abs + offset);
-          acc_s[kb][i] = vis ? acc_s[kb][i] : -INFINITY;
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) acc_s[kb][i] = 0.f;
+        const int key = 32 * kb + col;
+  #pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8_t kfrag =
+              __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(kb_base + tile_off(key, 2 * ks + half)));
+          acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qv[ks], acc_s[kb], 0, 0, 0);
         }
       }
-    }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, acc_s[kb][i]);
-    tmax = max_xor32(tmax) * a.c;  // log2 units
-    // The exponent reference moves only when the tile maximum exceeds it by
-    // more than kTau; otherwise the weights stay <= 2^kTau and the output
-    // needs no rescale. The branch is taken when any row of the wave moves.
-    const bool grow = tmax > m_run + kTau;
-    if (__ballot(grow)) {
-      const float alpha = grow ? fast_exp2(m_run - tmax) : 1.f;  // 0 while the old reference is -inf
-      m_run = grow ? tmax : m_run;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
-    }
-    const float neg_ref = m_run == -INFINITY ? 0.f : -m_run;
-    float psum = 0.f;
-    uint32_t pk[2][8];  // P^T operand, packed bf16 pairs
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float p0 = fast_exp2(fmaf(acc_s[kb][i], a.c, neg_ref));
-        const float p1 = fast_exp2(fmaf(acc_s[kb][i + 1], a.c, neg_ref));
-        psum += p0 + p1;
-        pk[kb][i >> 1] = pack_bf16x2(p0, p1);
-      }
-    }
-    l_run += psum;
 
-    // ---- O^T += V^T P^T : 4 blocks of 32 dims, 4 steps of 16 keys ----
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t* src = &pk[ks >> 1][(ks & 1) * 4];
-      const u32x4_t pw = {src[0], src[1], src[2], src[3]};
-      const bf16x8_t pfrag = __builtin_bit_cast(bf16x8_t, pw);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint16_t* vp = lds_vt + (32 * db + col) * kVStride + 16 * ks + 8 * half;
-        const bf16x8_t vfrag = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(vp));
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag, pfrag, acc_o[db], 0, 0, 0);
+      // ---- mask, online softmax (row = this lane's query row) ----
+      // element i of block kb is key 32kb + 8(i/4) + 4half + i%4 of the tile.
+      // The maximum is taken on raw scores (c > 0); the scale is folded into
+      // the exponent argument.
+      const bool need_mask = (t0 + kBN > ctx) || (a.causal && t0 + kBN - 1 > r0 + offset);
+      if (need_mask) {
+  #pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = t0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+            const bool vis = key < ctx && (!a.causal || key <= row_abs + offset);
+            acc_s[kb][i] = vis ? acc_s[kb][i] : -INFINITY;
+          }
+        }
       }
-    }
+      float mx[2];
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float m0 = fmaxf(fmaxf(acc_s[kb][0], acc_s[kb][1]), acc_s[kb][2]);
+        const float m1 = fmaxf(fmaxf(acc_s[kb][3], acc_s[kb][4]), acc_s[kb][5]);
+        const float m2 = fmaxf(fmaxf(acc_s[kb][6], acc_s[kb][7]), acc_s[kb][8]);
+        const float m3 = fmaxf(fmaxf(acc_s[kb][9], acc_s[kb][10]), acc_s[kb][11]);
+        const float m4 = fmaxf(fmaxf(acc_s[kb][12], acc_s[kb][13]), acc_s[kb][14]);
+        mx[kb] = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), acc_s[kb][15]));
+      }
+      const float tmax = max_xor32(fmaxf(mx[0], mx[1])) * a.c;  // log2 units
+      // The exponent reference moves only when the tile maximum exceeds it by
+      // more than kTau; otherwise the weights stay <= 2^kTau and the output
+      // needs no rescale. The branch is taken when any row of the wave moves.
+      const bool grow = tmax > m_run + kTau;
+      if (__ballot(grow)) {
+        const float alpha = grow ? fast_exp2(m_run - tmax) : 1.f;  // 0 while the old reference is -inf
+        m_run = grow ? tmax : m_run;
+        l_run *= alpha;
+  #pragma unroll
+        for (int db = 0; db < 4; ++db)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
+      }
+      const float neg_ref = m_run == -INFINITY ? 0.f : -m_run;
+      uint32_t pk[2][8];  // P^T operand, packed bf16 pairs
+      float psum = 0.f;
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+  #pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = fast_exp2(fmaf(acc_s[kb][i], a.c, neg_ref));
+          const float p1 = fast_exp2(fmaf(acc_s[kb][i + 1], a.c, neg_ref));
+          pk[kb][i >> 1] = pack_bf16x2(p0, p1);
+          psum = dot2_bf16(pk[kb][i >> 1], ones_bf16x2, psum);  // the weights the MFMA uses
+        }
+      }
+      l_run += psum;
+
+      // ---- O^T += V^T P^T : 4 blocks of 32 dims, 4 steps of 16 keys ----
+  #pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint32_t* src = &pk[ks >> 1][(ks & 1) * 4];
+        const u32x4_t pw = {src[0], src[1], src[2], src[3]};
+        const bf16x8_t pfrag = __builtin_bit_cast(bf16x8_t, pw);
+        const int key0 = 16 * ks + vk_lane;
+  #pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int c = 4 * db + vc_lane;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vb_base + tile_off(key0, c) + vb_lane));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vb_base + tile_off(key0 + 8, c) + vb_lane));
+          const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
+          const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
+          const u32x4_t vw = {lw.x, lw.y, hw.x, hw.y};
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pfrag, acc_o[db], 0, 0, 0);
+        }
+      }
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile_step(t, lds_k0, lds_v0, lds_k1, lds_v1);
+    if (t + 1 < n_tiles) tile_step(t + 1, lds_k1, lds_v1, lds_k0, lds_v0);
   }
+  wait_all_loads();  // no load may still be writing this work item's LDS at exit
 
   // ---- finalize: divide by the row sum, store bf16 ----
   if (!wave_has_rows) return;
