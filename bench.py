@@ -127,6 +127,44 @@ class Case:
         return start.elapsed_time(stop) / steps, wall / steps * 1e3
 
 
+class AppendCase:
+    """The K/V append of ``new_len`` tokens per sequence into a problem's pools (the write half)."""
+
+    def __init__(self, p, new_len: int, copies: int):
+        import numpy as np
+        import torch
+        from paged_flashattention_kv_amd import native
+        from paged_flashattention_kv_amd import workloads as wl
+
+        dev = "cuda:0"
+        rng = np.random.Generator(np.random.PCG64(1000 + p.seed))
+
+        def bf(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        shape = (p.batch, p.num_kv_heads, new_len, p.head_dim)
+        kn = bf(wl.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32)))
+        vn = bf(wl.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32)))
+        # sources rotated so that repeats are not served by the Infinity Cache
+        self.src = [(kn, vn)] + [(kn.clone(), vn.clone()) for _ in range(copies - 1)]
+        self.k = bf(p.key_pages)
+        self.v = bf(p.value_pages)
+        self.bt = torch.from_numpy(p.block_table).to(dev)
+        self.ctx = torch.from_numpy(p.context_lens).to(dev)
+        self.p = p
+        self.i = 0
+        self._native = native
+        # bytes the method must move: every new K and V byte read once and written once
+        self.bytes = 2 * 2 * p.batch * p.num_kv_heads * new_len * p.head_dim * 2
+
+    def step(self):
+        kn, vn = self.src[self.i % len(self.src)]
+        self.i += 1
+        self._native.kv_append(kn, vn, self.k, self.v, self.bt, self.ctx, self.p.page_size)
+
+    time = Case.time
+
+
 def cpu_baseline(p, min_seconds: float):
     """float64 oracle on whole passes over the workload; TB/s over the same algorithmic bytes."""
     import oracle
@@ -276,6 +314,22 @@ def main():
         }
         del c5
         torch.cuda.empty_cache()
+        for name, cfg, new_len, copies in (("kv_append_prefill", "long_prefill", 2048, 8),
+                                           ("kv_append_decode", "decode_batch", 1, 8)):
+            pa = wl.make_config(cfg)
+            ca = AppendCase(pa, new_len, copies)
+            msa, _ = ca.time(max(20, args.steps // 4), max(5, args.warmup // 4))
+            ga = ca.bytes / (msa * 1e-3) / 1e9
+            extra[name] = {
+                "workload": f"append {new_len} new token(s) per sequence into the {cfg} pools "
+                            f"(B={pa.batch} H_kv={pa.num_kv_heads} D=128, page_size={pa.page_size})",
+                "ms_per_step": round(msa, 5), "value": round(ga / 1e3, 4), "unit": "TB/s",
+                "roofline": {"bound": "hbm", "achieved": round(ga, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(ga / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_kv_append",
+                             "algorithmic_bytes_per_launch": ca.bytes},
+            }
+            del ca
+            torch.cuda.empty_cache()
         result["extra"] = extra
 
     if not args.no_cpu_baseline:

@@ -159,6 +159,38 @@ int paged_attention_check_metadata(const int32_t* block_table, const int32_t* co
                                    int32_t page_size, int32_t query_len, int32_t causal,
                                    void* stream);
 
+/*
+ * paged_kv_append -- writes the keys and values of new_len new tokens per
+ * sequence into their page slots: the write half of the paged cache
+ * ("Week 3 Day 5: Paged FlashAttention": logical position -> block_table ->
+ * page and slot; the causal decode that follows a paged prefill needs the
+ * new token's K/V in its page before paged_attention runs).
+ *   key_new, value_new  bf16 [batch, num_kv_heads, new_len, head_dim], device
+ *   key_pages, value_pages  bf16 [num_pages, num_kv_heads, page_size, head_dim],
+ *                device, updated in place: only the new tokens' slots are
+ *                written
+ *   block_table  int32 [batch, max_pages], device
+ *   context_lens int32 [batch], device: the context length AFTER the append,
+ *                so token l of sequence b goes to logical position
+ *                context_lens[b] - new_len + l (the convention paged_attention
+ *                uses for query rows)
+ * Device-data preconditions (not checked, but broken ones never cause a stray
+ * write: a sequence with context_lens[b] < new_len is skipped, and so is a
+ * token whose position falls past the block table or whose page id is not
+ * a page of the pool):
+ * new_len <= context_lens[b] <= max_pages * page_size; block_table[b, j] is
+ * a page of the pool for every j the new positions touch; no two (sequence,
+ * position) pairs of one call map to the same page slot.
+ * The new K/V buffers must not overlap the pools, nor the two pools each
+ * other. Asynchronous on `stream`; nothing is allocated. Returns PA_OK,
+ * PA_ERR_INVALID, PA_ERR_UNSUPPORTED (head_dim != 128) or PA_ERR_LAUNCH;
+ * nothing is launched unless every check passes.
+ */
+int paged_kv_append(const void* key_new, const void* value_new, void* key_pages, void* value_pages,
+                    const int32_t* block_table, const int32_t* context_lens, int32_t batch,
+                    int32_t num_kv_heads, int32_t new_len, int32_t head_dim, int32_t num_pages,
+                    int32_t page_size, int32_t max_pages, void* stream);
+
 /* Message describing the last error returned on the calling thread ("" if none). */
 const char* paged_attention_last_error(void);
 

@@ -16,6 +16,8 @@ on the CPU" (nanoserve), "Week 2 Day 5: Fused Decode Attention" (tiny-llm)):
 - ``online.paged_attention_online`` -- a float64 tile-streaming model of the
   fused loop (masked tile load through the block table, separate -inf score
   mask, running max / denominator / weighted-V fold).
+- ``append.kv_append_ref`` -- the write half: new tokens' K/V copied into
+  their page slots through the same translation.
 
 Pins (tests marked ``not gpu``) tie these to brute force, a library special
 case (torch scaled-dot-product attention in float64), closed forms and
@@ -32,8 +34,10 @@ from .reference import (
 )
 from .brute import paged_attention_brute
 from .online import paged_attention_online, tile_plan
+from .append import kv_append_ref
 
 __all__ = [
+    "kv_append_ref",
     "bf16_bits_to_f64",
     "gather_history",
     "kv_head_of",

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libpagedattn.so")
 
-SOURCES = ["pa_plan.cpp", "paged_attention.cpp", "pa_decode.hip", "pa_prefill.hip"]
+SOURCES = ["pa_plan.cpp", "paged_attention.cpp", "pa_decode.hip", "pa_prefill.hip", "pa_append.hip"]
 ARCH = "gfx950"
 
 

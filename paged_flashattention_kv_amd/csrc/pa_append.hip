@@ -1,0 +1,91 @@
+// pa_append.hip -- the write half of the paged K/V cache for gfx950: the
+// keys and values of L new tokens per sequence go to their page slots
+// through the same translation the attention kernels read with
+// ("Week 3 Day 5: Paged FlashAttention": logical position -> block_table ->
+// page, slot; the causal decode that follows a paged prefill needs the new
+// token's K/V in its page first).
+//
+// Token l of sequence b sits at logical position s = context_lens[b] - L + l
+// (context_lens counts the tokens after the append, the same convention the
+// attention kernels use for query rows). Its K row for kv head h is copied
+// to key_pages[block_table[b][s / page_size], h, s % page_size, :], and the
+// same for V. HBM-bound: every new byte is read once and written once.
+//
+// Layout: one 256-byte row per 16 lanes (16 bytes each); a 256-thread work
+// item moves 16 rows of K and 16 of V. Rows are ordered (sequence, kv head,
+// token), so the reads are contiguous and consecutive tokens of one page
+// land in consecutive 256-byte slots. Broken metadata never turns into a
+// stray write: a sequence whose context is shorter than its new tokens is
+// skipped, and so is a row whose position falls past the block table or
+// whose page id is not a page of the pool.
+
+#include "pa_device.h"
+#include "pa_kernels.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerItem = kThreads / 16;
+
+struct AppendArgs {
+  const uint16_t* key_new;
+  const uint16_t* value_new;
+  uint16_t* key_pages;
+  uint16_t* value_pages;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int64_t rows;  // batch * num_kv_heads * new_len
+  int num_kv_heads, new_len, num_pages, page_size, ps_log2, max_pages;
+};
+
+__global__ void __launch_bounds__(kThreads) pa_kv_append(AppendArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerItem + (threadIdx.x >> 4);
+  if (row >= a.rows) return;
+  const int chunk = threadIdx.x & 15;
+  const int l = (int)(row % a.new_len);
+  const int64_t bh = row / a.new_len;
+  const int h = (int)(bh % a.num_kv_heads);
+  const int b = (int)(bh / a.num_kv_heads);
+  const int ctx = a.context_lens[b];
+  if (ctx < a.new_len) return;  // the sequence cannot hold its new tokens: none is written
+  const int s = ctx - a.new_len + l;
+  const int lp = a.ps_log2 >= 0 ? (s >> a.ps_log2) : s / a.page_size;
+  if (lp >= a.max_pages) return;
+  const int32_t page = a.block_table[(size_t)b * a.max_pages + lp];
+  if (page < 0 || page >= a.num_pages) return;
+  const int slot = s - lp * a.page_size;
+  const size_t src = (size_t)row * 128 + chunk * 8;
+  const size_t dst = (((size_t)page * a.num_kv_heads + h) * a.page_size + slot) * 128 + chunk * 8;
+  const u32x4_t k = *reinterpret_cast<const u32x4_t*>(a.key_new + src);
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.value_new + src);
+  *reinterpret_cast<u32x4_t*>(a.key_pages + dst) = k;
+  *reinterpret_cast<u32x4_t*>(a.value_pages + dst) = v;
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendKernelArgs& k, hipStream_t stream) {
+  AppendArgs a;
+  a.key_new = static_cast<const uint16_t*>(k.key_new);
+  a.value_new = static_cast<const uint16_t*>(k.value_new);
+  a.key_pages = static_cast<uint16_t*>(k.key_pages);
+  a.value_pages = static_cast<uint16_t*>(k.value_pages);
+  a.block_table = k.block_table;
+  a.context_lens = k.context_lens;
+  a.rows = (int64_t)k.batch * k.num_kv_heads * k.new_len;
+  a.num_kv_heads = k.num_kv_heads;
+  a.new_len = k.new_len;
+  a.num_pages = k.num_pages;
+  a.page_size = k.page_size;
+  a.ps_log2 = -1;
+  for (int e = 0; e < 31; ++e)
+    if ((1 << e) == k.page_size) a.ps_log2 = e;
+  a.max_pages = k.max_pages;
+  const int64_t items = (a.rows + kRowsPerItem - 1) / kRowsPerItem;
+  hipLaunchKernelGGL(pa_kv_append, dim3((unsigned)items), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

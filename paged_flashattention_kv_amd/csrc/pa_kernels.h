@@ -29,4 +29,17 @@ hipError_t launch_decode(const KernelArgs& k, const Plan& p, hipStream_t stream)
 // Long-query bf16-MFMA tiled schedule (pa_prefill.hip).
 hipError_t launch_prefill(const KernelArgs& k, const Plan& p, hipStream_t stream);
 
+struct AppendKernelArgs {
+  const void* key_new;
+  const void* value_new;
+  void* key_pages;
+  void* value_pages;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int batch, num_kv_heads, new_len, num_pages, page_size, max_pages;
+};
+
+// Writes new tokens' K/V into their page slots (pa_append.hip).
+hipError_t launch_append(const AppendKernelArgs& k, hipStream_t stream);
+
 }  // namespace pa

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <string>
@@ -186,6 +187,47 @@ int paged_attention_check_metadata(const int32_t* block_table, const int32_t* co
                                               "] = " + std::to_string(p) + " is not a page of the pool");
     }
   }
+  g_last_error.clear();
+  return PA_OK;
+}
+
+int paged_kv_append(const void* key_new, const void* value_new, void* key_pages, void* value_pages,
+                    const int32_t* block_table, const int32_t* context_lens, int32_t batch,
+                    int32_t num_kv_heads, int32_t new_len, int32_t head_dim, int32_t num_pages,
+                    int32_t page_size, int32_t max_pages, void* stream) {
+  if (!key_new || !value_new || !key_pages || !value_pages || !block_table || !context_lens)
+    return set_error(PA_ERR_INVALID, "a tensor pointer is NULL");
+  if (batch < 1 || num_kv_heads < 1 || new_len < 1 || head_dim < 1 || num_pages < 1 || page_size < 1 ||
+      max_pages < 1)
+    return set_error(PA_ERR_INVALID, "all sizes must be positive");
+  if (head_dim != pa::kHeadDim) return set_error(PA_ERR_UNSUPPORTED, "only head_dim == 128 is implemented");
+  const int64_t max_ctx = int64_t(max_pages) * page_size;
+  if (max_ctx > INT32_MAX) return set_error(PA_ERR_UNSUPPORTED, "max_pages * page_size exceeds int32");
+  if (max_ctx < new_len) return set_error(PA_ERR_INVALID, "max_pages * page_size < new_len");
+  const int64_t rows = int64_t(batch) * num_kv_heads * new_len;
+  if (rows > (int64_t(1) << 35)) return set_error(PA_ERR_UNSUPPORTED, "batch * num_kv_heads * new_len too large");
+  const size_t new_bytes = size_t(rows) * head_dim * 2;
+  const size_t pool_bytes = size_t(num_pages) * num_kv_heads * page_size * head_dim * 2;
+  if (overlaps(key_pages, pool_bytes, value_pages, pool_bytes))
+    return set_error(PA_ERR_INVALID, "key_pages and value_pages overlap");
+  if (overlaps(key_new, new_bytes, key_pages, pool_bytes) || overlaps(key_new, new_bytes, value_pages, pool_bytes) ||
+      overlaps(value_new, new_bytes, key_pages, pool_bytes) || overlaps(value_new, new_bytes, value_pages, pool_bytes))
+    return set_error(PA_ERR_INVALID, "new K/V overlap a page pool");
+  pa::AppendKernelArgs k;
+  k.key_new = key_new;
+  k.value_new = value_new;
+  k.key_pages = key_pages;
+  k.value_pages = value_pages;
+  k.block_table = block_table;
+  k.context_lens = context_lens;
+  k.batch = batch;
+  k.num_kv_heads = num_kv_heads;
+  k.new_len = new_len;
+  k.num_pages = num_pages;
+  k.page_size = page_size;
+  k.max_pages = max_pages;
+  const hipError_t e = pa::launch_append(k, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, std::string("launch failed: ") + hipGetErrorString(e));
   g_last_error.clear();
   return PA_OK;
 }

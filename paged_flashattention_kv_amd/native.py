@@ -37,6 +37,7 @@ EXPORTED = (
     "paged_attention_schedule",
     "paged_attention_check_metadata",
     "paged_attention_last_error",
+    "paged_kv_append",
 )
 
 _lib = None
@@ -75,6 +76,8 @@ def load() -> ctypes.CDLL:
         lib.paged_attention_schedule.restype = ctypes.c_int
         lib.paged_attention_check_metadata.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp]
         lib.paged_attention_check_metadata.restype = ctypes.c_int
+        lib.paged_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+        lib.paged_kv_append.restype = ctypes.c_int
         lib.paged_attention_last_error.argtypes = []
         lib.paged_attention_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -192,6 +195,50 @@ def paged_attention(
     )
     _check(rc)
     return out
+
+
+def kv_append(
+    key_new: torch.Tensor,
+    value_new: torch.Tensor,
+    key_pages: torch.Tensor,
+    value_pages: torch.Tensor,
+    block_table: torch.Tensor,
+    context_lens: torch.Tensor,
+    page_size: int,
+    *,
+    stream: Optional[torch.cuda.Stream] = None,
+) -> None:
+    """Writes new tokens' K/V into their page slots, in place ("Week 3 Day 5: Paged FlashAttention").
+
+    key_new / value_new [B, H_kv, L_new, D] bf16; key_pages / value_pages
+    [num_pages, H_kv, page_size, D] bf16 (updated); block_table [B,
+    max_pages] int32; context_lens [B] int32 = context lengths after the
+    append, so token l of sequence b goes to position context_lens[b] -
+    L_new + l. Asynchronous on ``stream`` (default: the current stream).
+    """
+    dev = key_new.device
+    if dev.type != "cuda":
+        raise ValueError("key_new must be a GPU tensor")
+    _require(key_new, "key_new", torch.bfloat16, 4, dev)
+    _require(value_new, "value_new", torch.bfloat16, 4, dev)
+    _require(key_pages, "key_pages", torch.bfloat16, 4, dev)
+    _require(value_pages, "value_pages", torch.bfloat16, 4, dev)
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(context_lens, "context_lens", torch.int32, 1, dev)
+    B, Hkv, L, D = key_new.shape
+    P, Hp, ps, Dp = key_pages.shape
+    if tuple(value_new.shape) != tuple(key_new.shape) or tuple(value_pages.shape) != tuple(key_pages.shape):
+        raise ValueError("keys and values must have matching shapes")
+    if ps != page_size or Dp != D or Hp != Hkv:
+        raise ValueError("page pool shape does not match page_size / kv heads / head_dim")
+    if block_table.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_table and context_lens need one row per sequence")
+    rc = load().paged_kv_append(
+        key_new.data_ptr(), value_new.data_ptr(), key_pages.data_ptr(), value_pages.data_ptr(),
+        block_table.data_ptr(), context_lens.data_ptr(), B, Hkv, L, D, P, ps, block_table.shape[1],
+        _stream_ptr(stream, dev),
+    )
+    _check(rc)
 
 
 def check_metadata(block_table: torch.Tensor, context_lens: torch.Tensor, num_pages: int, page_size: int,

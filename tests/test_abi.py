@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "paged_attention.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(paged_attention\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(paged_\w*)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -31,7 +31,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 7
+    assert len(names) == 8
     assert sorted(native.EXPORTED) == names
     raw = ctypes.CDLL(native.LIB_PATH)
     for n in names:
@@ -74,6 +74,35 @@ def _call(lib, **kw):
 )
 def test_invalid_arguments_return_codes(lib, kw, code):
     assert _call(lib, **kw) == code
+    assert native.last_error() != ""
+
+
+def _append(lib, **kw):
+    a = dict(kn=FAKE, vn=FAKE + 0x100000, kp=FAKE + 0x200000, vp=FAKE + 0x300000, bt=FAKE + 0x400000,
+             cl=FAKE + 0x500000, B=2, Hkv=2, L=3, D=128, P=8, ps=16, mp=4)
+    a.update(kw)
+    return lib.paged_kv_append(a["kn"], a["vn"], a["kp"], a["vp"], a["bt"], a["cl"], a["B"], a["Hkv"], a["L"],
+                               a["D"], a["P"], a["ps"], a["mp"], None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(kn=None), native.PA_ERR_INVALID),
+        (dict(vp=None), native.PA_ERR_INVALID),
+        (dict(cl=None), native.PA_ERR_INVALID),
+        (dict(B=0), native.PA_ERR_INVALID),
+        (dict(L=0), native.PA_ERR_INVALID),
+        (dict(ps=0), native.PA_ERR_INVALID),
+        (dict(D=64), native.PA_ERR_UNSUPPORTED),
+        (dict(L=65, ps=16, mp=4), native.PA_ERR_INVALID),  # 65 new tokens cannot fit 4 pages of 16
+        (dict(mp=1 << 20, ps=1 << 12), native.PA_ERR_UNSUPPORTED),  # positions past int32
+        (dict(vp=FAKE + 0x200000 + 4096), native.PA_ERR_INVALID),  # the two pools overlap
+        (dict(kn=FAKE + 0x200000), native.PA_ERR_INVALID),  # new keys inside the key pool
+    ],
+)
+def test_append_invalid_arguments_return_codes(lib, kw, code):
+    assert _append(lib, **kw) == code
     assert native.last_error() != ""
 
 
