@@ -41,6 +41,7 @@ POOL_COPIES = 3
 KERNEL_SOURCES = {
     "pa_decode_work": ["paged_flashattention_kv_amd/csrc/pa_decode.hip", "paged_flashattention_kv_amd/csrc/pa_device.h"],
     "pa_prefill_mfma": ["paged_flashattention_kv_amd/csrc/pa_prefill.hip", "paged_flashattention_kv_amd/csrc/pa_device.h"],
+    "pa_kv_append": ["paged_flashattention_kv_amd/csrc/pa_append.hip", "paged_flashattention_kv_amd/csrc/pa_device.h"],
 }
 
 
@@ -325,7 +326,8 @@ def main():
                             f"(B={pa.batch} H_kv={pa.num_kv_heads} D=128, page_size={pa.page_size})",
                 "ms_per_step": round(msa, 5), "value": round(ga / 1e3, 4), "unit": "TB/s",
                 "roofline": {"bound": "hbm", "achieved": round(ga, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                             "frac": round(ga / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_kv_append",
+                             "frac": round(ga / HBM_PEAK_GBPS, 4),
+                             "traffic": measured_traffic("pa_kv_append", name), "kernel": "pa_kv_append",
                              "algorithmic_bytes_per_launch": ca.bytes},
             }
             del ca
