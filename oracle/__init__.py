@@ -18,6 +18,9 @@ on the CPU" (nanoserve), "Week 2 Day 5: Fused Decode Attention" (tiny-llm)):
   mask, running max / denominator / weighted-V fold).
 - ``append.kv_append_ref`` -- the write half: new tokens' K/V copied into
   their page slots through the same translation.
+- ``varlen.paged_attention_varlen_ref`` -- a mixed batch (each sequence its
+  own query length, queries packed token-major): the definition applied to
+  every sequence on its own.
 
 Pins (tests marked ``not gpu``) tie these to brute force, a library special
 case (torch scaled-dot-product attention in float64), closed forms and
@@ -35,9 +38,12 @@ from .reference import (
 from .brute import paged_attention_brute
 from .online import paged_attention_online, tile_plan
 from .append import kv_append_ref
+from .varlen import paged_attention_varlen_ref, validate_varlen
 
 __all__ = [
     "kv_append_ref",
+    "paged_attention_varlen_ref",
+    "validate_varlen",
     "bf16_bits_to_f64",
     "gather_history",
     "kv_head_of",

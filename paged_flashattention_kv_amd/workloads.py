@@ -325,3 +325,209 @@ def repack_pages(p: PagedProblem, new_page_size: int, seed: int) -> PagedProblem
             k[dst, :, s % new_page_size, :] = p.key_pages[src, :, s % ps, :]
             v[dst, :, s % new_page_size, :] = p.value_pages[src, :, s % ps, :]
     return dataclasses.replace(p, key_pages=k, value_pages=v, block_table=table, page_size=new_page_size)
+
+
+@dataclasses.dataclass
+class VarlenProblem:
+    """A mixed batch: every sequence has its own number of query rows.
+
+    ``query`` is packed token-major, uint16 bf16 bits ``[T, H_q, D]``;
+    sequence b owns tokens ``[query_start[b], query_start[b + 1])``
+    (``query_start`` int32 ``[B + 1]``). The pool, table and context lengths
+    are laid out as in :class:`PagedProblem`.
+    """
+
+    name: str
+    query: np.ndarray
+    key_pages: np.ndarray
+    value_pages: np.ndarray
+    block_table: np.ndarray
+    context_lens: np.ndarray
+    query_start: np.ndarray
+    page_size: int
+    scale: float
+    causal: bool
+    seed: int
+
+    @property
+    def batch(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def total_query(self) -> int:
+        return int(self.query.shape[0])
+
+    @property
+    def num_q_heads(self) -> int:
+        return int(self.query.shape[1])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.query.shape[2])
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.key_pages.shape[1])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.key_pages.shape[0])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def query_lens(self) -> np.ndarray:
+        return np.diff(self.query_start.astype(np.int64))
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max()) if self.batch else 0
+
+    def kv_bytes(self) -> int:
+        """K+V bytes the method must read: every position of a sequence with queries, once."""
+        ctx = self.context_lens.astype(np.int64)[self.query_lens > 0]
+        return int(ctx.sum()) * self.num_kv_heads * self.head_dim * 2 * 2
+
+    def visible_pairs(self) -> int:
+        total = 0
+        for L, c in zip(self.query_lens.tolist(), self.context_lens.tolist()):
+            if L == 0:
+                continue
+            total += L * (c - L) + L * (L + 1) // 2 if self.causal else L * c
+        return total
+
+    def flops(self) -> int:
+        """Algorithmic FLOPs: 2*D for Q.K and 2*D for P.V per visible pair per q head."""
+        return 4 * self.head_dim * self.num_q_heads * self.visible_pairs()
+
+
+def make_varlen_problem(
+    seed: int,
+    num_q_heads: int,
+    num_kv_heads: int,
+    head_dim: int,
+    page_size: int,
+    lens: Union[Sequence[Sequence[int]], Callable[[np.random.Generator], Sequence[Sequence[int]]]],
+    pool_pages: Optional[int] = None,
+    causal: bool = True,
+    scale: Optional[float] = None,
+    poison: bool = False,
+    name: str = "custom_varlen",
+    max_pages: Optional[int] = None,
+) -> VarlenProblem:
+    """Draw one mixed batch.
+
+    ``lens`` is ``(query_lens, context_lens)`` -- two equal-length lists --
+    or a function of the generator returning them (drawn first). The rest of
+    the draw order is that of :func:`make_problem`: page permutation, q, k,
+    v. ``poison`` fills unused pages and slots past each context end with
+    bf16 NaN.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ql, cl = lens(rng) if callable(lens) else lens
+    ql = np.asarray(ql, dtype=np.int64)
+    ctx = np.asarray(cl, dtype=np.int64)
+    if ql.shape != ctx.shape or ql.ndim != 1:
+        raise ValueError("query_lens and context_lens must be equal-length lists")
+    batch = int(ctx.shape[0])
+    pages_per_seq = [int(math.ceil(c / page_size)) for c in ctx.tolist()]
+    needed = int(sum(pages_per_seq))
+    if pool_pages is None:
+        pool_pages = max(needed, 1)
+    if pool_pages < needed:
+        raise ValueError("pool too small")
+    width = max(max(pages_per_seq, default=1), 1) if max_pages is None else int(max_pages)
+    perm = rng.permutation(pool_pages).astype(np.int32)
+    table = np.full((batch, width), -1, dtype=np.int32)
+    pos = 0
+    for b, n in enumerate(pages_per_seq):
+        table[b, :n] = perm[pos:pos + n]
+        pos += n
+    qs = np.zeros(batch + 1, dtype=np.int64)
+    qs[1:] = np.cumsum(ql)
+    T = int(qs[-1])
+    q = _normal_bf16(rng, (T, num_q_heads, head_dim))
+    k = _normal_bf16(rng, (pool_pages, num_kv_heads, page_size, head_dim))
+    v = _normal_bf16(rng, (pool_pages, num_kv_heads, page_size, head_dim))
+    if poison:
+        used = np.zeros(pool_pages, dtype=bool)
+        for b, n in enumerate(pages_per_seq):
+            if n == 0:
+                continue
+            used[table[b, :n]] = True
+            tail = int(ctx[b]) - (n - 1) * page_size
+            if tail < page_size:
+                last = table[b, n - 1]
+                k[last, :, tail:, :] = BF16_NAN
+                v[last, :, tail:, :] = BF16_NAN
+        k[~used] = BF16_NAN
+        v[~used] = BF16_NAN
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(head_dim)))
+    return VarlenProblem(
+        name=name,
+        query=q,
+        key_pages=k,
+        value_pages=v,
+        block_table=table,
+        context_lens=ctx.astype(np.int32),
+        query_start=qs.astype(np.int32),
+        page_size=int(page_size),
+        scale=float(np.float32(scale)),
+        causal=bool(causal),
+        seed=int(seed),
+    )
+
+
+def _serving_step(n: int, n_prefill: int, chunk: int, prompt, output):
+    """Lengths of one continuous-batching step: n sequences, n_prefill of them
+    prefilling one ``chunk``-token step of a prompt, the rest decoding one token.
+
+    Prompt lengths ~ U[prompt], generated lengths ~ U[output]. A prefilling
+    sequence is at a random chunk of its prompt (the last chunk may be
+    shorter); a decoding one has its whole prompt plus some generated tokens
+    (at least one: the token being decoded). Prefilling sequences sit at
+    random places in the batch.
+    """
+
+    def draw(rng: np.random.Generator):
+        ql = np.ones(n, dtype=np.int64)
+        cl = np.empty(n, dtype=np.int64)
+        pre = rng.permutation(n)[:n_prefill]
+        is_pre = np.zeros(n, dtype=bool)
+        is_pre[pre] = True
+        for b in range(n):
+            p = int(rng.integers(prompt[0], prompt[1] + 1))
+            if is_pre[b]:
+                k = int(rng.integers(0, (p + chunk - 1) // chunk))
+                end = min((k + 1) * chunk, p)
+                ql[b] = end - k * chunk
+                cl[b] = end
+            else:
+                cl[b] = p + int(rng.integers(max(output[0], 1), output[1] + 1))
+        return ql, cl
+
+    return draw
+
+
+# name -> (seed, keyword arguments of make_varlen_problem)
+VARLEN_CONFIGS: Dict[str, dict] = {
+    # One continuous-batching step at the Qwen3-4B attention shape with the
+    # serving trace's length mix (prompts U[128, 1024], outputs U[32, 128],
+    # 128-token prefill steps), widened to 64 sequences: 8 prefill one chunk,
+    # 56 decode one token. 128-token shuffled pages.
+    "mixed_batch": dict(
+        seed=6, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=128,
+        lens=_serving_step(64, 8, 128, (128, 1024), (32, 128)), causal=True,
+    ),
+}
+
+
+def make_varlen_config(name: str, poison: bool = False, **overrides) -> VarlenProblem:
+    """Draw a named mixed batch (``overrides`` replace arguments)."""
+    kw = dict(VARLEN_CONFIGS[name])
+    kw.update(overrides)
+    seed = kw.pop("seed")
+    return make_varlen_problem(seed=seed, poison=poison, name=name, **kw)
