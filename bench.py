@@ -166,6 +166,67 @@ class AppendCase:
     time = Case.time
 
 
+class VarlenCase:
+    """A mixed batch (per-sequence query lengths) through paged_attention_varlen, pools rotated."""
+
+    def __init__(self, p, copies: int):
+        import numpy as np
+        import torch
+        from paged_flashattention_kv_amd import native
+
+        dev = "cuda:0"
+
+        def bf(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.p = p
+        self.q = bf(p.query)
+        k = bf(p.key_pages)
+        v = bf(p.value_pages)
+        self.pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(copies - 1)]
+        self.bt = torch.from_numpy(p.block_table).to(dev)
+        self.ctx = torch.from_numpy(p.context_lens).to(dev)
+        self.qs = torch.from_numpy(p.query_start).to(dev)
+        self.out = torch.empty_like(self.q)
+        need = native.varlen_workspace_bytes(p.batch, p.num_q_heads, p.num_kv_heads, p.max_query_len, p.head_dim,
+                                             p.page_size, p.max_pages)
+        self.ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+        self.i = 0
+        self._native = native
+
+    def step(self):
+        k, v = self.pools[self.i % len(self.pools)]
+        self.i += 1
+        self._native.paged_attention_varlen(self.q, k, v, self.bt, self.ctx, self.qs, self.p.max_query_len,
+                                            self.p.page_size, self.p.scale, self.p.causal, out=self.out,
+                                            workspace=self.ws)
+
+    time = Case.time
+
+
+def mixed_roofline_us(p) -> dict:
+    """Lower bound of one mixed-batch call on this chip: the decode part's K/V bytes at HBM peak plus the
+    prefill part's flops at the bf16 matrix peak (the two launches run one after the other)."""
+    import numpy as np
+
+    ql = p.query_lens
+    group = p.num_q_heads // p.num_kv_heads
+    if group * p.max_query_len <= 8:
+        dec_max = p.max_query_len
+    else:
+        dec_max = 1 if group <= 8 else 0
+    dec = (ql >= 1) & (ql <= dec_max)
+    pre = ql > dec_max
+    ctx = p.context_lens.astype(np.int64)
+    dec_bytes = int(ctx[dec].sum()) * p.num_kv_heads * p.head_dim * 4
+    pre_pairs = 0
+    for L, c in zip(ql[pre].tolist(), ctx[pre].tolist()):
+        pre_pairs += L * (c - L) + L * (L + 1) // 2 if p.causal else L * c
+    pre_flops = 4 * p.head_dim * p.num_q_heads * pre_pairs
+    t = dec_bytes / (HBM_PEAK_GBPS * 1e9) + pre_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    return {"decode_kv_bytes": dec_bytes, "prefill_flops": pre_flops, "bound_us": round(t * 1e6, 3)}
+
+
 def cpu_baseline(p, min_seconds: float):
     """float64 oracle on whole passes over the workload; TB/s over the same algorithmic bytes."""
     import oracle
@@ -332,6 +393,24 @@ def main():
             }
             del ca
             torch.cuda.empty_cache()
+        pm = wl.make_varlen_config("mixed_batch")
+        cm = VarlenCase(pm, 8)
+        msm, _ = cm.time(max(20, args.steps // 2), max(5, args.warmup // 2))
+        rl = mixed_roofline_us(pm)
+        extra["mixed_batch"] = {
+            "workload": f"mixed_batch: B={pm.batch}, {int((pm.query_lens > 1).sum())} prefill chunks (<=128 tokens) "
+                        f"+ {int((pm.query_lens == 1).sum())} one-token decodes, T={pm.total_query} H_q=32 H_kv=8 "
+                        f"D=128, prompts U[128,1024] outputs U[32,128] (seed 6), page_size=128 shuffled",
+            "ms_per_step": round(msm, 5),
+            "tokens_per_s": round(pm.total_query / (msm * 1e-3), 1),
+            "kv_tbps": round(pm.kv_bytes() / (msm * 1e-3) / 1e12, 4),
+            "tflops": round(pm.flops() / (msm * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "hbm+mfma", "bound_us": rl["bound_us"], "achieved_us": round(msm * 1e3, 2),
+                         "frac": round(rl["bound_us"] / (msm * 1e3), 4), "decode_kv_bytes": rl["decode_kv_bytes"],
+                         "prefill_flops": rl["prefill_flops"], "kernels": ["pa_decode_work", "pa_prefill_mfma"]},
+        }
+        del cm
+        torch.cuda.empty_cache()
         result["extra"] = extra
 
     if not args.no_cpu_baseline:

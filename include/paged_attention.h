@@ -191,6 +191,97 @@ int paged_kv_append(const void* key_new, const void* value_new, void* key_pages,
                     int32_t num_kv_heads, int32_t new_len, int32_t head_dim, int32_t num_pages,
                     int32_t page_size, int32_t max_pages, void* stream);
 
+/*
+ * paged_attention_varlen -- the operator over a mixed batch in which every
+ * sequence has its own number of query rows: prefill chunks and one-token
+ * decodes in one call (the continuous-batching step that "Week 3 Day 5:
+ * Paged FlashAttention", Task 4, measures on its serving trace; there the
+ * dispatch picks the tiled prefill schedule for long queries and the vector
+ * decode schedule for short ones -- here that choice is made per sequence).
+ *
+ *   query        bf16 [total_query, num_q_heads, head_dim], packed
+ *                token-major: sequence b owns tokens
+ *                [query_start[b], query_start[b + 1])
+ *   query_start  int32 [batch + 1], device; L_b = query_start[b + 1] -
+ *                query_start[b] is sequence b's query length (0 allowed:
+ *                the sequence is skipped and its context is never read)
+ *   out          bf16 [total_query, num_q_heads, head_dim], row t written
+ *                once for every t of a sequence with L_b >= 1
+ *   max_query_len  host bound on every L_b, 1 <= max_query_len <=
+ *                total_query (sizes the prefill grid; no device read)
+ *   key_pages, value_pages, block_table, context_lens, scale, causal: as for
+ *                paged_attention; query row l of sequence b sits at logical
+ *                position context_lens[b] - L_b + l.
+ *   workspace    at least paged_attention_varlen_workspace_bytes(...) bytes,
+ *                zero-filled once before first use (as for paged_attention).
+ *
+ * total_query == 0 is a valid empty call: nothing is enqueued, and query /
+ * out may then be NULL.
+ *
+ * Device-data preconditions (not checked; see
+ * paged_attention_varlen_check_metadata): query_start[0] == 0,
+ * non-decreasing, query_start[batch] == total_query, every L_b <=
+ * max_query_len; for each b with L_b >= 1 the preconditions of
+ * paged_attention with query_len = L_b. A sequence whose offsets fall
+ * outside [0, total_query] or whose length exceeds max_query_len is skipped
+ * (its rows are not written), so broken offsets never cause a stray access.
+ *
+ * Dispatch, with group = num_q_heads / num_kv_heads: when group *
+ * max_query_len <= 8 every sequence runs the decode schedule (the rule of
+ * paged_attention); otherwise one-token queries run the decode schedule
+ * (none when group > 8) and every longer query the prefill schedule -- the
+ * decode schedule's cost grows with its widest sequence's rows. Two launches
+ * on `stream`, the second only when some query is longer than the decode
+ * bound.
+ */
+int paged_attention_varlen(const void* query, const void* key_pages, const void* value_pages,
+                           const int32_t* block_table, const int32_t* context_lens, const int32_t* query_start,
+                           void* out, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t total_query, int32_t max_query_len, int32_t head_dim, int32_t num_pages,
+                           int32_t page_size, int32_t max_pages, float scale, int32_t causal, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attention_varlen_ex -- paged_attention_varlen with the split between
+ * the two schedules and the decode work items chosen by the caller (tests run
+ * one mixed batch through different splits; tuning sweeps).
+ *   decode_max_len     -1: automatic (as paged_attention_varlen); 0: every
+ *                      sequence takes the prefill schedule; k >= 1:
+ *                      sequences with L_b <= k take the decode schedule,
+ *                      which needs k * num_q_heads / num_kv_heads <= 8.
+ *   decode_work_items  as for paged_attention_ex (0 = automatic).
+ */
+int paged_attention_varlen_ex(const void* query, const void* key_pages, const void* value_pages,
+                              const int32_t* block_table, const int32_t* context_lens,
+                              const int32_t* query_start, void* out, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t total_query, int32_t max_query_len,
+                              int32_t head_dim, int32_t num_pages, int32_t page_size, int32_t max_pages,
+                              float scale, int32_t causal, void* workspace, size_t workspace_bytes,
+                              int32_t decode_max_len, int32_t decode_work_items, void* stream);
+
+/*
+ * Workspace bytes paged_attention_varlen_ex needs for these sizes and
+ * choices (decode_max_len = -1 and decode_work_items = 0 for
+ * paged_attention_varlen); 0 when none is needed, (size_t)-1 if invalid.
+ * Pure host arithmetic.
+ */
+size_t paged_attention_varlen_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t max_query_len, int32_t head_dim, int32_t page_size,
+                                              int32_t max_pages, int32_t decode_max_len,
+                                              int32_t decode_work_items);
+
+/*
+ * paged_attention_varlen_check_metadata -- opt-in debug check of the
+ * mixed-batch preconditions above (copies the three index arrays to the
+ * host on `stream` and synchronises it). Returns PA_OK, PA_ERR_INVALID,
+ * PA_ERR_LAUNCH or PA_ERR_METADATA with the first offending entry in
+ * paged_attention_last_error().
+ */
+int paged_attention_varlen_check_metadata(const int32_t* block_table, const int32_t* context_lens,
+                                          const int32_t* query_start, int32_t batch, int32_t max_pages,
+                                          int32_t num_pages, int32_t page_size, int32_t total_query,
+                                          int32_t max_query_len, int32_t causal, void* stream);
+
 /* Message describing the last error returned on the calling thread ("" if none). */
 const char* paged_attention_last_error(void);
 

@@ -84,6 +84,11 @@ struct DecodeArgs {
   float* ws_ml;      // [work_items][2][rows][2]   partial (reference max, sum)
   float* ws_acc;     // [work_items][2][rows][128] partial unnormalised outputs
   uint32_t epoch;    // differs from the previous call's and from 0
+  // Packed mixed batch: query/out [total_query, H_q, 128], sequence b owns
+  // tokens [qstart[b], qstart[b + 1]) and is served here when its length is
+  // 1 .. query_len. nullptr: the uniform [B, H_q, query_len, 128] layout.
+  const int32_t* qstart;
+  int total_query;
   int batch, num_q_heads, num_kv_heads, query_len, group, rows;
   int page_size, ps_log2, max_pages;
   int work_items;
@@ -237,17 +242,45 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 // Wait until this wave's memory operations (stores included) have completed.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ int64_t n_gran(int ctx) { return (ctx + kGran - 1) / kGran; }
+__device__ __forceinline__ int64_t n_gran(int ctx) { return ctx > 0 ? (ctx + kGran - 1) / kGran : 0; }
+
+// Query rows of sequence b that this launch serves (0: none), and for a
+// packed batch the token of its first row. A packed sequence whose offsets
+// fall outside [0, total_query] or whose length is not 1 .. query_len is
+// not served (no row of it is read or written).
+__device__ __forceinline__ int seq_rows(const DecodeArgs& a, int b, int& start) {
+  start = 0;
+  if (a.qstart == nullptr) return a.query_len;
+  const int s0 = a.qstart[b], s1 = a.qstart[b + 1];
+  if (s0 < 0 || s1 > a.total_query || s1 <= s0 || s1 - s0 > a.query_len) return 0;
+  start = s0;
+  return s1 - s0;
+}
+
+// Granules of sequence b's K/V per kv head that this launch streams.
+__device__ __forceinline__ int64_t seq_gran(const DecodeArgs& a, int b) {
+  int start;
+  return seq_rows(a, b, start) > 0 ? n_gran(a.context_lens[b]) : 0;
+}
+
+// Element offset of query (and output) row l of head h of sequence b, which
+// has L rows starting at token `start`.
+__device__ __forceinline__ size_t row_off(const DecodeArgs& a, int b, int start, int L, int h, int l) {
+  return a.qstart ? ((size_t)(start + l) * a.num_q_heads + h) * 128
+                  : (((size_t)b * a.num_q_heads + h) * L + l) * 128;
+}
 
 // Work item w covers granules [w * total / work_items, (w + 1) * total / work_items).
 __device__ __forceinline__ int64_t gran_begin(int64_t w, int64_t total, int64_t items) { return w * total / items; }
 
-// One piece: keys [k0, k1) of segment (b, kvh). Leaves the merged state in
-// LDS-free registers of the caller's work item and stores it.
+// One piece: keys [k0, k1) of segment (b, kvh), for the group * L query
+// rows of that kv head (sequence b has L rows from token `start`). Merges
+// the 4 waves' states and either stores the output (the piece is the whole
+// segment) or leaves the partial state in the workspace slot.
 template <int ROWS, bool ALIGNED>
 __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_bt, float (*lds_m)[ROWS],
                                              float (*lds_l)[ROWS], float (*lds_acc)[ROWS][128], int b, int kvh,
-                                             int ctx, int k0, int k1, bool direct, int slot) {
+                                             int ctx, int L, int start, int k0, int k1, bool direct, int slot) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -255,19 +288,20 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
   const int dc = lane & 7;
 
   // Query rows of this kv head: row r -> q head kvh*group + r / L, position r % L.
+  const int rows = a.group * L;
   uint32_t q[ROWS][8];
   int last[ROWS];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    if (r < a.rows) {
-      const int h = kvh * a.group + r / a.query_len;
-      const int l = r % a.query_len;
-      const uint16_t* qp = a.query + (((size_t)b * a.num_q_heads + h) * a.query_len + l) * 128;
+    if (r < rows) {
+      const int h = kvh * a.group + r / L;
+      const int l = r % L;
+      const uint16_t* qp = a.query + row_off(a, b, start, L, h, l);
       const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(qp + dc * 8);
       const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(qp + 64 + dc * 8);
       q[r][0] = lo.x; q[r][1] = lo.y; q[r][2] = lo.z; q[r][3] = lo.w;
       q[r][4] = hi.x; q[r][5] = hi.y; q[r][6] = hi.z; q[r][7] = hi.w;
-      last[r] = a.causal ? l + ctx - a.query_len : ctx - 1;
+      last[r] = a.causal ? l + ctx - L : ctx - 1;
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) q[r][j] = 0u;
@@ -365,7 +399,7 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
   }
   __syncthreads();
   const size_t part = ((size_t)blockIdx.x * 2 + slot) * a.rows;
-  for (int idx = tid; idx < a.rows * 128; idx += kThreads) {
+  for (int idx = tid; idx < rows * 128; idx += kThreads) {
     const int r = idx >> 7;
     const int d = idx & 127;
     float mw[kWaves];
@@ -383,10 +417,9 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
       num = fmaf(f, lds_acc[w][r][d], num);
     }
     if (direct) {
-      const int h = kvh * a.group + r / a.query_len;
-      const int l = r % a.query_len;
-      const size_t orow = ((size_t)b * a.num_q_heads + h) * a.query_len + l;
-      a.out[orow * 128 + d] = to_bf16(num / den);
+      const int h = kvh * a.group + r / L;
+      const int l = r % L;
+      a.out[row_off(a, b, start, L, h, l) + d] = to_bf16(num / den);
     } else {
       // device-coherent stores (no cache-wide fence needed; see arrive_last)
       store_coherent(a.ws_acc + (part + r) * 128 + d, num);
@@ -441,10 +474,10 @@ __device__ __forceinline__ SegmentItems segment_items(int64_t S, int64_t E, int6
 // dimensions in parallel). Work item w's piece sits in slot 0 when the
 // segment is the first piece of w's range, else in slot 1. Partials with
 // maximum -inf (no visible key) contribute 0.
-__device__ void merge_segment(const DecodeArgs& a, int b, int kvh, int64_t S, const SegmentItems& it,
-                              int64_t total) {
+__device__ void merge_segment(const DecodeArgs& a, int b, int kvh, int L, int start, int64_t S,
+                              const SegmentItems& it, int64_t total) {
   const int64_t P = a.work_items;
-  for (int idx = threadIdx.x; idx < a.rows * 128; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < a.group * L * 128; idx += kThreads) {
     const int r = idx >> 7;
     const int d = idx & 127;
     float M = -INFINITY;
@@ -464,10 +497,9 @@ __device__ void merge_segment(const DecodeArgs& a, int b, int kvh, int64_t S, co
       den = fmaf(f, load_coherent(a.ws_ml + part * 2 + 1), den);
       num = fmaf(f, load_coherent(a.ws_acc + part * 128 + d), num);
     }
-    const int h = kvh * a.group + r / a.query_len;
-    const int l = r % a.query_len;
-    const size_t orow = ((size_t)b * a.num_q_heads + h) * a.query_len + l;
-    a.out[orow * 128 + d] = to_bf16(num / den);
+    const int h = kvh * a.group + r / L;
+    const int l = r % L;
+    a.out[row_off(a, b, start, L, h, l) + d] = to_bf16(num / den);
   }
 }
 
@@ -486,7 +518,7 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
   const int chunk = (a.batch + kThreads - 1) / kThreads;
   const int c0 = min(a.batch, tid * chunk), c1 = min(a.batch, c0 + chunk);
   int64_t mine = 0;
-  for (int b = c0; b < c1; ++b) mine += n_gran(a.context_lens[b]);
+  for (int b = c0; b < c1; ++b) mine += seq_gran(a, b);
   lds_scan[tid] = mine;
   __syncthreads();
   for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan
@@ -505,7 +537,7 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
     // which sequence holds granule G0
     int64_t pref = excl;
     for (int b = c0; b < c1; ++b) {
-      const int64_t ng = n_gran(a.context_lens[b]);
+      const int64_t ng = seq_gran(a, b);
       if (G0 >= pref * a.num_kv_heads && G0 < (pref + ng) * a.num_kv_heads) {
         lds_start[0] = b;
         lds_start[1] = pref;
@@ -522,7 +554,13 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
   int nth = 0;
   while (G < G1) {
     const int ctx = a.context_lens[b];
-    const int64_t ng = n_gran(ctx);
+    int start;
+    const int L = seq_rows(a, b, start);
+    const int64_t ng = L > 0 ? n_gran(ctx) : 0;
+    if (ng == 0) {  // nothing of sequence b in the granule order
+      ++b;
+      continue;
+    }
     const int64_t base = pref * a.num_kv_heads;  // first granule of sequence b
     const int kvh = (int)((G - base) / ng);
     const int64_t S = base + kvh * ng, E = S + ng;
@@ -530,7 +568,8 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
     const int k0 = (int)((G - S) * kGran);
     const int k1 = (int)min((gend - S) * kGran, (int64_t)ctx);
     const bool direct = G == S && gend == E;
-    decode_piece<ROWS, ALIGNED>(a, lds_bt, lds_m, lds_l, lds_acc, b, kvh, ctx, k0, k1, direct, nth == 0 ? 0 : 1);
+    decode_piece<ROWS, ALIGNED>(a, lds_bt, lds_m, lds_l, lds_acc, b, kvh, ctx, L, start, k0, k1, direct,
+                                nth == 0 ? 0 : 1);
     if (!direct) {
       // publish this piece, then the last of the segment's work items merges it
       wait_stores();
@@ -538,7 +577,7 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
       const SegmentItems it = segment_items(S, E, total, a.work_items);
       if (tid == 0) lds_last = arrive_last(a.ws_ctr + (size_t)b * a.num_kv_heads + kvh, a.epoch, it.count);
       __syncthreads();
-      if (lds_last) merge_segment(a, b, kvh, S, it, total);
+      if (lds_last) merge_segment(a, b, kvh, L, start, S, it, total);
     }
     G = gend;
     ++nth;
@@ -609,6 +648,9 @@ hipError_t launch_decode(const KernelArgs& k, const Plan& p, hipStream_t stream)
   a.c = k.scale * kLog2e;
   a.causal = k.causal;
   a.epoch = k.epoch;
+  a.qstart = k.query_start;
+  a.total_query = k.total_query;
+  if (k.query_start) a.query_len = k.dec_max_len;  // the longest query this launch serves
   const size_t lds = (size_t)p.bt_entries * sizeof(int32_t);
   hipError_t e;
   switch (p.rows_pad) {

@@ -21,6 +21,15 @@ struct KernelArgs {
   float scale;
   int causal;
   uint32_t epoch;  // per-call tag of the decode arrival counters (never 0)
+  // Mixed batch: query and out are packed token-major [total_query, H_q, D]
+  // and sequence b owns tokens [query_start[b], query_start[b + 1]);
+  // query_len is then the longest query of the batch. The decode launch
+  // serves sequences with 1 <= L_b <= dec_max_len, the prefill launch those
+  // with L_b > dec_max_len. query_start == nullptr: the uniform layout
+  // [B, H_q, query_len, D], every sequence served by the one launch.
+  const int32_t* query_start = nullptr;
+  int total_query = 0;
+  int dec_max_len = 0;
 };
 
 // Short-query split-context schedule (pa_decode.hip).

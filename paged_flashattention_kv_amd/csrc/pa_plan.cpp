@@ -1,6 +1,7 @@
 // pa_plan.cpp -- validation and launch planning (host only, no HIP).
 #include "pa_plan.h"
 
+#include <algorithm>
 #include <climits>
 
 namespace pa {
@@ -80,6 +81,48 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
     if (p.num_work > INT32_MAX) return fail(err, kErrUnsupported, "prefill grid too large");
   }
   *plan = p;
+  if (err) err->clear();
+  return kOk;
+}
+
+int make_plan_varlen(const Shape& s, int decode_max_len, int decode_work_items, bool check_pool,
+                     VarlenPlan* plan, std::string* err) {
+  // the checks every part shares (sizes, GQA ratio, head_dim) come from make_plan
+  Plan probe;
+  int rc = make_plan(s, kSchedulePrefill, 0, check_pool, &probe, err);
+  if (rc != kOk) return rc;
+  const int group = probe.group;
+  VarlenPlan v;
+  if (decode_max_len < -1) return fail(err, kErrInvalid, "decode_max_len must be -1 (auto), 0 or positive");
+  if (decode_work_items < 0 || decode_work_items > kDecodeMaxWork)
+    return fail(err, kErrInvalid, "decode_work_items must be in [0, 65536]");
+  if (decode_max_len == -1) {
+    // Every query fits one decode work item: the uniform rule. Otherwise only
+    // one-token queries take the decode schedule: its cost grows with the
+    // rows of its widest sequence (2.2x from 4 to 8 rows, measured), so a
+    // 2-token query would slow every decode of the batch.
+    if (int64_t(group) * s.query_len <= kDecodeMaxRows)
+      v.dec_max_len = int(s.query_len);
+    else
+      v.dec_max_len = group <= kDecodeMaxRows ? 1 : 0;
+  } else {
+    if (int64_t(decode_max_len) * group > kDecodeMaxRows)
+      return fail(err, kErrInvalid, "decode_max_len * num_q_heads / num_kv_heads must be <= 8");
+    v.dec_max_len = int(std::min<int64_t>(decode_max_len, s.query_len));
+  }
+  if (v.dec_max_len > 0) {
+    Shape sd = s;
+    sd.query_len = v.dec_max_len;
+    rc = make_plan(sd, kScheduleDecode, decode_work_items, check_pool, &v.dec, err);
+    if (rc != kOk) return rc;
+    v.run_decode = true;
+    v.workspace_bytes = v.dec.workspace_bytes;
+  }
+  if (s.query_len > v.dec_max_len) {
+    v.pre = probe;
+    v.run_prefill = true;
+  }
+  *plan = v;
   if (err) err->clear();
   return kOk;
 }

@@ -54,10 +54,30 @@ constexpr int kErrInvalid = -1;
 constexpr int kErrUnsupported = -2;
 constexpr int kErrWorkspace = -3;
 
+// A mixed batch (per-sequence query lengths, queries packed token-major):
+// sequences with 1 <= L_b <= dec_max_len run the decode schedule, longer
+// ones the prefill schedule, as two launches on one stream.
+struct VarlenPlan {
+  int dec_max_len = 0;
+  bool run_decode = false;
+  bool run_prefill = false;
+  Plan dec;  // decode part: rows = group * dec_max_len (the workspace slot stride)
+  Plan pre;  // prefill part: query tiles cover max_query_len
+  size_t workspace_bytes = 0;
+};
+
 // Validates `s` and fills `plan`. `schedule` is 0 (auto), 1 (decode) or
 // 2 (prefill); `decode_work_items` is 0 (auto) or an explicit number of
 // decode work items. Returns kOk or a negative code with a message in `err`.
 int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_pool, Plan* plan,
               std::string* err);
+
+// Plans a mixed batch. `s.query_len` is the longest query of the batch
+// (max_query_len). `decode_max_len` is -1 (auto: max_query_len when
+// group * max_query_len <= 8, else 1 when group <= 8, else 0), 0 (every
+// sequence takes the prefill schedule) or an explicit bound with
+// group * decode_max_len <= 8.
+int make_plan_varlen(const Shape& s, int decode_max_len, int decode_work_items, bool check_pool,
+                     VarlenPlan* plan, std::string* err);
 
 }  // namespace pa

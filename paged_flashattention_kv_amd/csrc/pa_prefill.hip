@@ -70,6 +70,11 @@ struct PrefillArgs {
   const int32_t* block_table;
   const int32_t* context_lens;
   uint16_t* out;
+  // Packed mixed batch: query/out [total_query, H_q, 128], sequence b owns
+  // tokens [qstart[b], qstart[b + 1]); only sequences with skip_len < L_b <=
+  // query_len are served here. nullptr: uniform [B, H_q, query_len, 128].
+  const int32_t* qstart;
+  int total_query, skip_len;
   int batch, num_q_heads, num_kv_heads, query_len, group, n_qtiles;
   int page_size, ps_log2, max_pages;
   float c;  // scale * log2(e)
@@ -171,10 +176,18 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
   const int qtile = a.n_qtiles - 1 - task / a.batch;
   const int head = kvh * G + g;
 
-  const int L = a.query_len;
+  int L = a.query_len, start = 0;
+  if (a.qstart) {
+    const int s0 = a.qstart[b], s1 = a.qstart[b + 1];
+    const int64_t len = (int64_t)s1 - s0;
+    if (s0 < 0 || s1 > a.total_query || len <= a.skip_len || len > a.query_len) return;
+    L = (int)len;
+    start = s0;
+  }
+  const int q0 = qtile * kBM;
+  if (q0 >= L) return;  // a query tile past this sequence's rows (uniform across the work item)
   const int ctx = a.context_lens[b];
   const int offset = ctx - L;  // query row l sits at logical position l + offset
-  const int q0 = qtile * kBM;
   const int tile_last_row = min(q0 + kBM, L) - 1;
   const int kv_end = a.causal ? min(ctx, tile_last_row + offset + 1) : ctx;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
@@ -201,7 +214,9 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
   bf16x8_t qv[8];
   {
     const int row = r0 + col;
-    const uint16_t* qp = a.query + (((size_t)b * a.num_q_heads + head) * L + (row < L ? row : 0)) * 128 + 8 * half;
+    const int rr = row < L ? row : 0;
+    const size_t qrow = a.qstart ? (size_t)(start + rr) * a.num_q_heads + head : ((size_t)b * a.num_q_heads + head) * L + rr;
+    const uint16_t* qp = a.query + qrow * 128 + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       u32x4_t w = u32x4_t{0u, 0u, 0u, 0u};
@@ -344,7 +359,9 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
   const float l_tot = sum_xor32(l_run);
   if (row_abs >= L) return;
   const float inv = 1.f / l_tot;
-  uint16_t* op = a.out + (((size_t)b * a.num_q_heads + head) * L + row_abs) * 128;
+  const size_t orow = a.qstart ? (size_t)(start + row_abs) * a.num_q_heads + head
+                               : ((size_t)b * a.num_q_heads + head) * L + row_abs;
+  uint16_t* op = a.out + orow * 128;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -378,6 +395,9 @@ hipError_t launch_prefill(const KernelArgs& k, const Plan& p, hipStream_t stream
   a.max_pages = k.max_pages;
   a.c = k.scale * kLog2e;
   a.causal = k.causal;
+  a.qstart = k.query_start;
+  a.total_query = k.total_query;
+  a.skip_len = k.query_start ? k.dec_max_len : 0;
   if (p.aligned)
     hipLaunchKernelGGL(pa_prefill_mfma<true>, dim3((unsigned)p.num_work), dim3(kThreads), 0, stream, a);
   else

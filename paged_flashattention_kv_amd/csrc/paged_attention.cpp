@@ -232,6 +232,146 @@ int paged_kv_append(const void* key_new, const void* value_new, void* key_pages,
   return PA_OK;
 }
 
+int paged_attention_varlen_ex(const void* query, const void* key_pages, const void* value_pages,
+                              const int32_t* block_table, const int32_t* context_lens,
+                              const int32_t* query_start, void* out, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t total_query, int32_t max_query_len,
+                              int32_t head_dim, int32_t num_pages, int32_t page_size, int32_t max_pages,
+                              float scale, int32_t causal, void* workspace, size_t workspace_bytes,
+                              int32_t decode_max_len, int32_t decode_work_items, void* stream) {
+  if (!key_pages || !value_pages || !block_table || !context_lens || !query_start)
+    return set_error(PA_ERR_INVALID, "a tensor pointer is NULL");
+  if (total_query < 0) return set_error(PA_ERR_INVALID, "total_query must be >= 0");
+  if (total_query > 0 && (!query || !out)) return set_error(PA_ERR_INVALID, "a tensor pointer is NULL");
+  if (causal != 0 && causal != 1) return set_error(PA_ERR_INVALID, "causal must be 0 or 1");
+  if (!std::isfinite(scale)) return set_error(PA_ERR_INVALID, "scale must be finite");
+  if (total_query > 0 && (max_query_len < 1 || max_query_len > total_query))
+    return set_error(PA_ERR_INVALID, "max_query_len must be in [1, total_query]");
+  pa::VarlenPlan plan;
+  std::string err;
+  const pa::Shape s = make_shape(batch, num_q_heads, num_kv_heads, total_query > 0 ? max_query_len : 1,
+                                 head_dim, num_pages, page_size, max_pages, causal != 0);
+  const int rc = pa::make_plan_varlen(s, decode_max_len, decode_work_items, true, &plan, &err);
+  if (rc != pa::kOk) return set_error(rc, err);
+  if (int64_t(total_query) * num_q_heads > INT32_MAX)
+    return set_error(PA_ERR_UNSUPPORTED, "total_query * num_q_heads exceeds int32");
+  if (total_query == 0) {  // no query rows: nothing to compute or write
+    g_last_error.clear();
+    return PA_OK;
+  }
+  if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
+    return set_error(PA_ERR_WORKSPACE, "workspace smaller than paged_attention_varlen_workspace_bytes() = " +
+                                           std::to_string(plan.workspace_bytes));
+  const size_t q_bytes = size_t(total_query) * num_q_heads * head_dim * 2;
+  const size_t pool_bytes = size_t(num_pages) * num_kv_heads * page_size * head_dim * 2;
+  if (overlaps(out, q_bytes, query, q_bytes) || overlaps(out, q_bytes, key_pages, pool_bytes) ||
+      overlaps(out, q_bytes, value_pages, pool_bytes) ||
+      overlaps(out, q_bytes, block_table, size_t(batch) * max_pages * 4) ||
+      overlaps(out, q_bytes, context_lens, size_t(batch) * 4) ||
+      overlaps(out, q_bytes, query_start, size_t(batch + 1) * 4) ||
+      (plan.workspace_bytes > 0 && overlaps(out, q_bytes, workspace, plan.workspace_bytes)))
+    return set_error(PA_ERR_INVALID, "out overlaps an input or the workspace");
+
+  pa::KernelArgs k;
+  k.query = query;
+  k.key_pages = key_pages;
+  k.value_pages = value_pages;
+  k.block_table = block_table;
+  k.context_lens = context_lens;
+  k.out = out;
+  k.workspace = workspace;
+  k.batch = batch;
+  k.num_q_heads = num_q_heads;
+  k.num_kv_heads = num_kv_heads;
+  k.query_len = max_query_len;
+  k.num_pages = num_pages;
+  k.page_size = page_size;
+  k.max_pages = max_pages;
+  k.scale = scale;
+  k.causal = causal;
+  k.epoch = next_epoch();
+  k.query_start = query_start;
+  k.total_query = total_query;
+  k.dec_max_len = plan.dec_max_len;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (plan.run_decode) e = pa::launch_decode(k, plan.dec, st);
+  if (e == hipSuccess && plan.run_prefill) e = pa::launch_prefill(k, plan.pre, st);
+  if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, std::string("launch failed: ") + hipGetErrorString(e));
+  g_last_error.clear();
+  return PA_OK;
+}
+
+int paged_attention_varlen(const void* query, const void* key_pages, const void* value_pages,
+                           const int32_t* block_table, const int32_t* context_lens, const int32_t* query_start,
+                           void* out, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t total_query, int32_t max_query_len, int32_t head_dim, int32_t num_pages,
+                           int32_t page_size, int32_t max_pages, float scale, int32_t causal, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return paged_attention_varlen_ex(query, key_pages, value_pages, block_table, context_lens, query_start, out,
+                                   batch, num_q_heads, num_kv_heads, total_query, max_query_len, head_dim,
+                                   num_pages, page_size, max_pages, scale, causal, workspace, workspace_bytes, -1,
+                                   0, stream);
+}
+
+size_t paged_attention_varlen_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t max_query_len, int32_t head_dim, int32_t page_size,
+                                              int32_t max_pages, int32_t decode_max_len,
+                                              int32_t decode_work_items) {
+  pa::VarlenPlan plan;
+  std::string err;
+  const pa::Shape s = make_shape(batch, num_q_heads, num_kv_heads, max_query_len, head_dim, 1, page_size,
+                                 max_pages, false);
+  const int rc = pa::make_plan_varlen(s, decode_max_len, decode_work_items, false, &plan, &err);
+  if (rc != pa::kOk) {
+    set_error(rc, err);
+    return static_cast<size_t>(-1);
+  }
+  g_last_error.clear();
+  return plan.workspace_bytes;
+}
+
+int paged_attention_varlen_check_metadata(const int32_t* block_table, const int32_t* context_lens,
+                                          const int32_t* query_start, int32_t batch, int32_t max_pages,
+                                          int32_t num_pages, int32_t page_size, int32_t total_query,
+                                          int32_t max_query_len, int32_t causal, void* stream) {
+  if (!block_table || !context_lens || !query_start) return set_error(PA_ERR_INVALID, "a tensor pointer is NULL");
+  if (batch < 1 || max_pages < 1 || num_pages < 1 || page_size < 1 || total_query < 0 || max_query_len < 0)
+    return set_error(PA_ERR_INVALID, "sizes must be positive (total_query and max_query_len may be 0)");
+  std::vector<int32_t> bt(size_t(batch) * max_pages), ctx(batch), qs(size_t(batch) + 1);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(bt.data(), block_table, bt.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(ctx.data(), context_lens, ctx.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(qs.data(), query_start, qs.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, std::string("copy failed: ") + hipGetErrorString(e));
+  if (qs[0] != 0 || qs[batch] != total_query)
+    return set_error(PA_ERR_METADATA, "query_start must start at 0 and end at total_query");
+  const int64_t max_ctx = int64_t(max_pages) * page_size;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t L = int64_t(qs[b + 1]) - qs[b];
+    const std::string at = "[" + std::to_string(b) + "]";
+    if (L < 0) return set_error(PA_ERR_METADATA, "query_start decreases at " + at);
+    if (L > max_query_len) return set_error(PA_ERR_METADATA, "query length of sequence " + at + " > max_query_len");
+    if (L == 0) continue;  // a sequence without query rows is never read
+    const int32_t c = ctx[b];
+    if (c < 1 || c > max_ctx)
+      return set_error(PA_ERR_METADATA, "context_lens" + at + " = " + std::to_string(c) +
+                                            " outside [1, max_pages * page_size]");
+    if (causal && c < L)
+      return set_error(PA_ERR_METADATA, "context_lens" + at + " < its query length under causal");
+    const int64_t used = (int64_t(c) + page_size - 1) / page_size;
+    for (int64_t j = 0; j < used; ++j) {
+      const int32_t p = bt[size_t(b) * max_pages + j];
+      if (p < 0 || p >= num_pages)
+        return set_error(PA_ERR_METADATA, "block_table" + at + "[" + std::to_string(j) + "] = " + std::to_string(p) +
+                                              " is not a page of the pool");
+    }
+  }
+  g_last_error.clear();
+  return PA_OK;
+}
+
 const char* paged_attention_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

@@ -38,6 +38,10 @@ EXPORTED = (
     "paged_attention_check_metadata",
     "paged_attention_last_error",
     "paged_kv_append",
+    "paged_attention_varlen",
+    "paged_attention_varlen_ex",
+    "paged_attention_varlen_workspace_bytes",
+    "paged_attention_varlen_check_metadata",
 )
 
 _lib = None
@@ -78,6 +82,15 @@ def load() -> ctypes.CDLL:
         lib.paged_attention_check_metadata.restype = ctypes.c_int
         lib.paged_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
         lib.paged_kv_append.restype = ctypes.c_int
+        var_args = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz]
+        lib.paged_attention_varlen.argtypes = var_args + [vp]
+        lib.paged_attention_varlen.restype = ctypes.c_int
+        lib.paged_attention_varlen_ex.argtypes = var_args + [i32, i32, vp]
+        lib.paged_attention_varlen_ex.restype = ctypes.c_int
+        lib.paged_attention_varlen_workspace_bytes.argtypes = [i32] * 9
+        lib.paged_attention_varlen_workspace_bytes.restype = sz
+        lib.paged_attention_varlen_check_metadata.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+        lib.paged_attention_varlen_check_metadata.restype = ctypes.c_int
         lib.paged_attention_last_error.argtypes = []
         lib.paged_attention_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -250,5 +263,108 @@ def check_metadata(block_table: torch.Tensor, context_lens: torch.Tensor, num_pa
     rc = load().paged_attention_check_metadata(
         block_table.data_ptr(), context_lens.data_ptr(), block_table.shape[0], block_table.shape[1],
         num_pages, page_size, query_len, 1 if causal else 0, _stream_ptr(stream, dev),
+    )
+    _check(rc)
+
+
+def varlen_workspace_bytes(batch, num_q_heads, num_kv_heads, max_query_len, head_dim, page_size, max_pages,
+                           decode_max_len=-1, decode_work_items=0) -> int:
+    n = load().paged_attention_varlen_workspace_bytes(batch, num_q_heads, num_kv_heads, max_query_len, head_dim,
+                                                      page_size, max_pages, decode_max_len, decode_work_items)
+    if n == ctypes.c_size_t(-1).value:
+        raise PagedAttentionError(PA_ERR_INVALID, last_error())
+    return int(n)
+
+
+def paged_attention_varlen(
+    query: torch.Tensor,
+    key_pages: torch.Tensor,
+    value_pages: torch.Tensor,
+    block_table: torch.Tensor,
+    context_lens: torch.Tensor,
+    query_start: torch.Tensor,
+    max_query_len: int,
+    page_size: int,
+    scale: Optional[float] = None,
+    causal: bool = True,
+    *,
+    out: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
+    decode_max_len: int = -1,
+    decode_work_items: int = 0,
+    stream: Optional[torch.cuda.Stream] = None,
+) -> torch.Tensor:
+    """Paged attention over a mixed batch: each sequence its own query length.
+
+    query [T, H_q, D] bf16 packed token-major, sequence b owning tokens
+    [query_start[b], query_start[b + 1]); query_start [B + 1] int32;
+    ``max_query_len`` a host bound on every sequence's query length (no
+    device read happens here). Pools, block_table, context_lens, scale and
+    causal as for :func:`paged_attention`; query row l of sequence b sits at
+    position context_lens[b] - L_b + l ("Week 3 Day 5: Paged
+    FlashAttention", Task 4: short queries take the decode schedule, long
+    ones the tiled prefill schedule -- chosen per sequence). Returns ``out``
+    [T, H_q, D] bf16. ``decode_max_len`` / ``decode_work_items``: see
+    paged_attention_varlen_ex in the C header.
+    """
+    dev = query.device
+    if dev.type != "cuda":
+        raise ValueError("query must be a GPU tensor")
+    _require(query, "query", torch.bfloat16, 3, dev)
+    _require(key_pages, "key_pages", torch.bfloat16, 4, dev)
+    _require(value_pages, "value_pages", torch.bfloat16, 4, dev)
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(context_lens, "context_lens", torch.int32, 1, dev)
+    _require(query_start, "query_start", torch.int32, 1, dev)
+    T, Hq, D = query.shape
+    P, Hkv, ps, Dk = key_pages.shape
+    B = context_lens.shape[0]
+    if tuple(value_pages.shape) != tuple(key_pages.shape):
+        raise ValueError("key_pages and value_pages must have the same shape")
+    if ps != page_size or Dk != D:
+        raise ValueError("page pool shape does not match page_size / head_dim")
+    if block_table.shape[0] != B or query_start.shape[0] != B + 1:
+        raise ValueError("block_table needs one row per sequence and query_start B + 1 entries")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty_like(query)
+    else:
+        _require(out, "out", torch.bfloat16, 3, dev)
+        if tuple(out.shape) != tuple(query.shape):
+            raise ValueError("out must have the query's shape")
+    if T == 0:
+        return out
+    need = varlen_workspace_bytes(B, Hq, Hkv, max_query_len, D, ps, max_pages, decode_max_len, decode_work_items)
+    ws_ptr, ws_len = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the query's device")
+        ws_ptr, ws_len = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rc = load().paged_attention_varlen_ex(
+        query.data_ptr(), key_pages.data_ptr(), value_pages.data_ptr(), block_table.data_ptr(),
+        context_lens.data_ptr(), query_start.data_ptr(), out.data_ptr(), B, Hq, Hkv, T, int(max_query_len), D, P,
+        ps, max_pages, float(scale), 1 if causal else 0, ws_ptr, ws_len, int(decode_max_len),
+        int(decode_work_items), _stream_ptr(stream, dev),
+    )
+    _check(rc)
+    return out
+
+
+def check_varlen_metadata(block_table: torch.Tensor, context_lens: torch.Tensor, query_start: torch.Tensor,
+                          num_pages: int, page_size: int, total_query: int, max_query_len: int,
+                          causal: bool = True, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Debug check of a mixed batch's device-side metadata (synchronises the stream)."""
+    dev = block_table.device
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(context_lens, "context_lens", torch.int32, 1, dev)
+    _require(query_start, "query_start", torch.int32, 1, dev)
+    rc = load().paged_attention_varlen_check_metadata(
+        block_table.data_ptr(), context_lens.data_ptr(), query_start.data_ptr(), block_table.shape[0],
+        block_table.shape[1], num_pages, page_size, total_query, max_query_len, 1 if causal else 0,
+        _stream_ptr(stream, dev),
     )
     _check(rc)

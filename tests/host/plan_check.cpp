@@ -75,6 +75,36 @@ int main() {
   // explicit work item counts size the workspace
   CHECK(pa::make_plan(shape(2, 8, 8, 1, 128, 16, 10), 1, 7, true, &p, &err) == pa::kOk);
   CHECK(p.work_items == 7 && p.work_cap == 7);
+  // mixed batches: which lengths take the decode schedule, and the parts' plans
+  pa::VarlenPlan v;
+  for (int maxL : {1, 2, 3, 8, 65, 128, 2048}) {
+    for (int G : {1, 2, 4, 8, 16}) {
+      CHECK(pa::make_plan_varlen(shape(5, 8 * G, 8, maxL, 128, 16, 300), -1, 0, true, &v, &err) == pa::kOk);
+      const int want = G * maxL <= 8 ? maxL : (G <= 8 ? 1 : 0);
+      CHECK(v.dec_max_len == want);
+      CHECK(v.run_decode == (want > 0) && v.run_prefill == (maxL > want));
+      if (v.run_decode) {
+        CHECK(v.dec.schedule == pa::kScheduleDecode && v.dec.rows == G * want && v.dec.rows_pad <= 8);
+        CHECK(v.workspace_bytes == v.dec.workspace_bytes && v.workspace_bytes > 0);
+      } else {
+        CHECK(v.workspace_bytes == 0);
+      }
+      if (v.run_prefill) CHECK(v.pre.schedule == pa::kSchedulePrefill && v.pre.n_qtiles == (maxL + 127) / 128);
+    }
+  }
+  CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 128, 128, 9), 0, 0, true, &v, &err) == pa::kOk);
+  CHECK(!v.run_decode && v.run_prefill && v.dec_max_len == 0 && v.workspace_bytes == 0);
+  CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 128, 128, 9), 1, 0, true, &v, &err) == pa::kOk);
+  CHECK(v.run_decode && v.run_prefill && v.dec_max_len == 1 && v.dec.rows == 4);
+  CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 128, 128, 9), 3, 0, true, &v, &err) == pa::kErrInvalid);
+  CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 128, 128, 9), -2, 0, true, &v, &err) == pa::kErrInvalid);
+  CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 128, 128, 9), -1, -1, true, &v, &err) == pa::kErrInvalid);
+  CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 128, 128, 9), -1, 70000, true, &v, &err) == pa::kErrInvalid);
+  CHECK(pa::make_plan_varlen(shape(64, 30, 8, 128, 128, 128, 9), -1, 0, true, &v, &err) == pa::kErrInvalid);
+  CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 96, 128, 9), -1, 0, true, &v, &err) == pa::kErrUnsupported);
+  // explicit decode work items reach the decode part
+  CHECK(pa::make_plan_varlen(shape(4, 32, 8, 1, 128, 16, 9), -1, 5, true, &v, &err) == pa::kOk);
+  CHECK(v.run_decode && !v.run_prefill && v.dec.work_items == 5 && v.dec.work_cap == 5);
   if (failures == 0) std::printf("plan_check: all passed\n");
   return failures == 0 ? 0 : 1;
 }

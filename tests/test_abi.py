@@ -31,7 +31,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 8
+    assert len(names) == 12
     assert sorted(native.EXPORTED) == names
     raw = ctypes.CDLL(native.LIB_PATH)
     for n in names:
@@ -104,6 +104,62 @@ def _append(lib, **kw):
 def test_append_invalid_arguments_return_codes(lib, kw, code):
     assert _append(lib, **kw) == code
     assert native.last_error() != ""
+
+
+def _varlen(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, bt=FAKE + 0x300000, cl=FAKE + 0x400000,
+             qs=FAKE + 0x480000, out=FAKE + 0x500000, B=2, Hq=4, Hkv=2, T=5, maxL=4, D=128, P=8, ps=16, mp=4,
+             scale=0.088, causal=1, ws=None, wsb=0, dml=-1, split=0)
+    a.update(kw)
+    return lib.paged_attention_varlen_ex(a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["out"], a["B"],
+                                         a["Hq"], a["Hkv"], a["T"], a["maxL"], a["D"], a["P"], a["ps"], a["mp"],
+                                         a["scale"], a["causal"], a["ws"], a["wsb"], a["dml"], a["split"], None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(qs=None), native.PA_ERR_INVALID),
+        (dict(bt=None), native.PA_ERR_INVALID),
+        (dict(q=None), native.PA_ERR_INVALID),  # NULL query is allowed only when T == 0
+        (dict(T=-1), native.PA_ERR_INVALID),
+        (dict(maxL=0), native.PA_ERR_INVALID),
+        (dict(maxL=6), native.PA_ERR_INVALID),  # longer than total_query
+        (dict(B=0), native.PA_ERR_INVALID),
+        (dict(Hq=3), native.PA_ERR_INVALID),
+        (dict(causal=2), native.PA_ERR_INVALID),
+        (dict(scale=float("inf")), native.PA_ERR_INVALID),
+        (dict(D=64), native.PA_ERR_UNSUPPORTED),
+        (dict(dml=5), native.PA_ERR_INVALID),  # 5 rows x group 2 > 8
+        (dict(dml=-2), native.PA_ERR_INVALID),
+        (dict(split=-1), native.PA_ERR_INVALID),
+        (dict(T=100, maxL=100, mp=4, ps=16), native.PA_ERR_INVALID),  # causal query longer than any context
+        (dict(out=FAKE + 2 * 4 * 128, dml=0), native.PA_ERR_INVALID),  # overlaps the query
+        (dict(out=FAKE + 0x480000 - 64, dml=0), native.PA_ERR_INVALID),  # overlaps query_start
+        (dict(), native.PA_ERR_WORKSPACE),  # length-1 sequences need the decode workspace
+    ],
+)
+def test_varlen_invalid_arguments_return_codes(lib, kw, code):
+    assert _varlen(lib, **kw) == code
+    assert native.last_error() != ""
+
+
+def test_varlen_empty_batch_is_a_no_op(lib):
+    assert _varlen(lib, q=None, out=None, T=0, maxL=0) == native.PA_OK
+    assert native.last_error() == ""
+
+
+def test_varlen_workspace(lib):
+    # a prefill chunk in the batch: only one-token queries take the decode part
+    n = native.varlen_workspace_bytes(64, 32, 8, 128, 128, 128, 9)
+    assert n == native.workspace_bytes(64, 32, 8, 1, 128, 128, 9, native.SCHEDULE_DECODE, 0)
+    # every query short enough for one decode work item: the uniform rule
+    assert native.varlen_workspace_bytes(64, 32, 8, 2, 128, 128, 9) == native.workspace_bytes(64, 32, 8, 2, 128, 128, 9)
+    assert native.varlen_workspace_bytes(64, 32, 8, 1, 128, 128, 9) == native.workspace_bytes(64, 32, 8, 1, 128, 128, 9)
+    assert native.varlen_workspace_bytes(64, 32, 8, 128, 128, 128, 9, decode_max_len=0) == 0
+    assert native.varlen_workspace_bytes(4, 64, 4, 128, 128, 128, 9) == 0  # group 16: no decode part
+    with pytest.raises(native.PagedAttentionError):
+        native.varlen_workspace_bytes(64, 32, 8, 128, 128, 128, 9, decode_max_len=3)
 
 
 def test_schedule_rule_and_workspace(lib):
