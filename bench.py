@@ -7,7 +7,9 @@ dispatcher picks) over one batch of synthetic input. The headline workload
 is the decode batch at the Qwen3-4B attention shape (B=64, H_q=32, H_kv=8,
 D=128, L=1, context lengths U[128, 4096] not tile multiples, 128-token
 pages shuffled over a pool sized to what the batch needs). Inputs are
-resident in HBM before the timed region. Three independent copies of the
+resident in HBM before the timed region. Each case first runs untimed for
+--prewarm-seconds (0.3 s) so the engine clock has settled, then W warmup
+calls, then exactly K timed calls. Three independent copies of the
 K/V page pool are rotated step by step so that the 256 MB Infinity Cache
 cannot serve repeated reads.
 
@@ -38,6 +40,7 @@ METRIC = "decode K/V TB/s (% HBM peak); causal prefill TFLOP/s (% bf16 MFMA peak
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 POOL_COPIES = 3
+PREWARM_SECONDS = 0.3  # untimed sustained load before each case's warmup calls (set by --prewarm-seconds)
 KERNEL_SOURCES = {
     "pa_decode_work": ["paged_flashattention_kv_amd/csrc/pa_decode.hip", "paged_flashattention_kv_amd/csrc/pa_device.h"],
     "pa_prefill_mfma": ["paged_flashattention_kv_amd/csrc/pa_prefill.hip", "paged_flashattention_kv_amd/csrc/pa_device.h"],
@@ -109,9 +112,20 @@ class Case:
                                      out=self.out, workspace=self.ws)
 
     def time(self, steps: int, warmup: int):
-        """ms per step over exactly ``steps`` calls, HIP events on the launch stream."""
+        """ms per step over exactly ``steps`` calls, HIP events on the launch stream.
+
+        Before the ``warmup`` calls the case runs untimed for PREWARM_SECONDS of
+        wall time: the engine clock of the GPU settles only after sustained load
+        (the first ~10 ms of a matrix-core-bound kernel run up to 20% slower),
+        so the timed calls see the steady state a serving loop runs in.
+        """
         import torch
 
+        t_end = time.perf_counter() + PREWARM_SECONDS
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                self.step()
+            torch.cuda.synchronize()
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
@@ -266,9 +280,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--prewarm-seconds", type=float, default=PREWARM_SECONDS,
+                    help="untimed sustained load before each case's warmup calls (the engine clock settles)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 1 GiB device copy (reference for counter scaling)")
     args = ap.parse_args()
+    globals()["PREWARM_SECONDS"] = max(0.0, args.prewarm_seconds)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this operator build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
