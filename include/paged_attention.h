@@ -51,7 +51,7 @@ enum {
   PA_OK = 0,
   PA_ERR_INVALID = -1,     /* null pointer, non-positive size, H_q % H_kv != 0,
                               max_pages * page_size < query_len, ... */
-  PA_ERR_UNSUPPORTED = -2, /* head_dim != 128, or a size past a kernel limit */
+  PA_ERR_UNSUPPORTED = -2, /* head_dim not 64, 128 or 256, or a size past a kernel limit */
   PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   PA_ERR_LAUNCH = -4,      /* the HIP runtime rejected a launch */
   PA_ERR_METADATA = -5     /* paged_attention_check_metadata found bad data */
@@ -96,8 +96,11 @@ enum {
  *
  * Dispatch (inside the library, "Week 3 Day 5", Task 4): a short query
  * (query_len * num_q_heads / num_kv_heads <= 8) runs the decode schedule,
- * anything longer the prefill schedule. Supported: head_dim == 128,
- * page_size >= 1, any batch, GQA ratio and context length that fit int32.
+ * anything longer the prefill schedule. Supported: head_dim 64, 128 or 256
+ * ("Week 3 Day 5", Task 1, writes its matrix kernel for head dim 128 and
+ * keeps generic controls for the rest; here both schedules are instantiated
+ * for each of the three), page_size >= 1, any batch, GQA ratio and context
+ * length that fit int32.
  */
 int paged_attention(const void* query, const void* key_pages, const void* value_pages,
                     const int32_t* block_table, const int32_t* context_lens, void* out,
@@ -183,7 +186,8 @@ int paged_attention_check_metadata(const int32_t* block_table, const int32_t* co
  * position) pairs of one call map to the same page slot.
  * The new K/V buffers must not overlap the pools, nor the two pools each
  * other. Asynchronous on `stream`; nothing is allocated. Returns PA_OK,
- * PA_ERR_INVALID, PA_ERR_UNSUPPORTED (head_dim != 128) or PA_ERR_LAUNCH;
+ * PA_ERR_INVALID, PA_ERR_UNSUPPORTED (head_dim not 64, 128 or 256) or
+ * PA_ERR_LAUNCH;
  * nothing is launched unless every check passes.
  */
 int paged_kv_append(const void* key_new, const void* value_new, void* key_pages, void* value_pages,

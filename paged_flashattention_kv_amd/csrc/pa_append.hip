@@ -11,10 +11,10 @@
 // to key_pages[block_table[b][s / page_size], h, s % page_size, :], and the
 // same for V. HBM-bound: every new byte is read once and written once.
 //
-// Layout: one 256-byte row per 16 lanes (16 bytes each); a 256-thread work
-// item moves 16 rows of K and 16 of V. Rows are ordered (sequence, kv head,
-// token), so the reads are contiguous and consecutive tokens of one page
-// land in consecutive 256-byte slots. Broken metadata never turns into a
+// Layout: one row of D bf16 values (2D bytes) per D/8 lanes, 16 bytes each;
+// a 256-thread work item moves 2048/D rows of K and as many of V (16 at head
+// dim 128). Rows are ordered (sequence, kv head, token), so the reads are
+// contiguous and consecutive tokens of one page land in consecutive slots. Broken metadata never turns into a
 // stray write: a sequence whose context is shorter than its new tokens is
 // skipped, and so is a row whose position falls past the block table or
 // whose page id is not a page of the pool.
@@ -27,7 +27,6 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerItem = kThreads / 16;
 
 struct AppendArgs {
   const uint16_t* key_new;
@@ -40,10 +39,14 @@ struct AppendArgs {
   int num_kv_heads, new_len, num_pages, page_size, ps_log2, max_pages;
 };
 
+// D/8 lanes copy one row of D bf16 values (16 bytes each).
+template <int D>
 __global__ void __launch_bounds__(kThreads) pa_kv_append(AppendArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerItem + (threadIdx.x >> 4);
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerItem = kThreads / kLanesPerRow;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerItem + threadIdx.x / kLanesPerRow;
   if (row >= a.rows) return;
-  const int chunk = threadIdx.x & 15;
+  const int chunk = threadIdx.x % kLanesPerRow;
   const int l = (int)(row % a.new_len);
   const int64_t bh = row / a.new_len;
   const int h = (int)(bh % a.num_kv_heads);
@@ -56,12 +59,20 @@ __global__ void __launch_bounds__(kThreads) pa_kv_append(AppendArgs a) {
   const int32_t page = a.block_table[(size_t)b * a.max_pages + lp];
   if (page < 0 || page >= a.num_pages) return;
   const int slot = s - lp * a.page_size;
-  const size_t src = (size_t)row * 128 + chunk * 8;
-  const size_t dst = (((size_t)page * a.num_kv_heads + h) * a.page_size + slot) * 128 + chunk * 8;
+  const size_t src = (size_t)row * D + chunk * 8;
+  const size_t dst = (((size_t)page * a.num_kv_heads + h) * a.page_size + slot) * D + chunk * 8;
   const u32x4_t k = *reinterpret_cast<const u32x4_t*>(a.key_new + src);
   const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.value_new + src);
   *reinterpret_cast<u32x4_t*>(a.key_pages + dst) = k;
   *reinterpret_cast<u32x4_t*>(a.value_pages + dst) = v;
+}
+
+template <int D>
+hipError_t launch_dim(const AppendArgs& a, hipStream_t stream) {
+  constexpr int kRowsPerItem = kThreads / (D / 8);
+  const int64_t items = (a.rows + kRowsPerItem - 1) / kRowsPerItem;
+  hipLaunchKernelGGL(pa_kv_append<D>, dim3((unsigned)items), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -83,9 +94,11 @@ hipError_t launch_append(const AppendKernelArgs& k, hipStream_t stream) {
   for (int e = 0; e < 31; ++e)
     if ((1 << e) == k.page_size) a.ps_log2 = e;
   a.max_pages = k.max_pages;
-  const int64_t items = (a.rows + kRowsPerItem - 1) / kRowsPerItem;
-  hipLaunchKernelGGL(pa_kv_append, dim3((unsigned)items), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  switch (k.head_dim) {
+    case 64: return launch_dim<64>(a, stream);
+    case 256: return launch_dim<256>(a, stream);
+    default: return launch_dim<128>(a, stream);
+  }
 }
 
 }  // namespace pa

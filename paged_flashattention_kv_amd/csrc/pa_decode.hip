@@ -26,11 +26,11 @@
 // Inside a piece: all query rows that read this kv head -- the GQA group
 // times the query length, at most 8 rows -- are served by ONE pass over the
 // piece's keys, so every K/V byte is read from HBM once per kv head. Waves
-// interleave 16-key steps. Lane layout inside a step: lane = 8 * kg + dc;
-// lane (kg, dc) holds key kg (and kg + 8) and head dims [8dc, 8dc+8) and
-// [64+8dc, 64+8dc+8): two 16-byte loads per key row, one load instruction
-// covering eight 128-byte row halves. q.k: packed bf16 dot products
-// (v_dot2_f32_bf16) summed over the key's 8 lanes with DPP. The exponent
+// interleave steps of 8 KB of K and V. Lane layout for head dim D (64, 128
+// or 256): LPK = D/16 lanes per key row, lane = LPK * kg + dc; lane (kg, dc)
+// holds key kg (and kg + 64/LPK) and head dims [8dc, 8dc+8) and
+// [D/2+8dc, D/2+8dc+8): two 16-byte loads per key row. q.k: packed bf16 dot
+// products (v_dot2_f32_bf16) summed over the key's LPK lanes with DPP. The exponent
 // reference is shared by the whole wave, so wave partials combine without
 // rescaling; the 4 waves merge in LDS through a common maximum. Register
 // stages rotate so the next steps' K/V loads are in flight while a step is
@@ -64,7 +64,16 @@ constexpr int kTK = PA_DECODE_TK;
 #define PA_DECODE_STAGES 3
 #endif
 constexpr int kStages = PA_DECODE_STAGES;
-constexpr int kStep = 8 * kTK;
+// Lane geometry for head dim D: D/16 lanes hold one key row (16 dims each,
+// two 16-byte chunks), so one load instruction covers 64/(D/16) key rows and
+// a wave step 8 KB of K and V whatever D is.
+template <int D>
+struct Geo {
+  static_assert(D == 64 || D == 128 || D == 256, "head dims 64, 128 and 256");
+  static constexpr int LPK = D / 16;         // lanes per key row
+  static constexpr int KPI = 64 / LPK;       // key rows per load instruction
+  static constexpr int kStep = KPI * kTK;    // keys per wave step
+};
 // The exponent reference of a row moves only when a tile's maximum exceeds it
 // by more than kTau (log2 units), so weights stay <= 2^kTau and the common
 // case needs no rescale of the accumulators.
@@ -112,43 +121,44 @@ struct Pager {
   int kg, dc;
 };
 
-// Page-translating load of one step: keys t0 + kg + 8i (i < kTK), dims
-// [8dc, 8dc+8) and [64+8dc, 64+8dc+8). Keys at or past the split end are
+// Page-translating load of one step: keys t0 + kg + KPI*i (i < kTK), dims
+// [8dc, 8dc+8) and [D/2+8dc, D/2+8dc+8). Keys at or past the split end are
 // redirected to the split's first key (always a valid row) so every load is
 // unconditional; their scores are masked to -inf and their weight is 0.
-template <bool ALIGNED>
+template <bool ALIGNED, int D>
 __device__ __forceinline__ void load_stage(const Pager& g, int t0, Stage& st) {
+  constexpr int KPI = Geo<D>::KPI;
   size_t row[kTK];
   if (ALIGNED) {
-    // page_size % 32 == 0 and t0 % 8kTK == 0: the step lies inside one page.
-    // A step wholly past the split end reads the split's first page instead.
+    // page_size % kStep == 0 and t0 % kStep == 0: the step lies inside one
+    // page. A step wholly past the split end reads the split's first page.
     const int tb = t0 < g.s1 ? t0 : g.s0;
     const int lp = div_ps(tb, g.page_size, g.ps_log2);
     const size_t base = (size_t)g.lds_bt[lp - g.lp0] * g.page_stride + g.head_off +
-                        (size_t)(tb - lp * g.page_size) * 128;
+                        (size_t)(tb - lp * g.page_size) * D;
 #pragma unroll
     for (int i = 0; i < kTK; ++i) {
-      const int key = t0 + g.kg + 8 * i;
-      row[i] = key < g.s1 ? base + (size_t)(g.kg + 8 * i) * 128 : base;
+      const int key = t0 + g.kg + KPI * i;
+      row[i] = key < g.s1 ? base + (size_t)(g.kg + KPI * i) * D : base;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < kTK; ++i) {
-      int key = t0 + g.kg + 8 * i;
+      int key = t0 + g.kg + KPI * i;
       key = key < g.s1 ? key : g.s0;
       const int lp = div_ps(key, g.page_size, g.ps_log2);
-      row[i] = (size_t)g.lds_bt[lp - g.lp0] * g.page_stride + g.head_off + (size_t)(key - lp * g.page_size) * 128;
+      row[i] = (size_t)g.lds_bt[lp - g.lp0] * g.page_stride + g.head_off + (size_t)(key - lp * g.page_size) * D;
     }
   }
 #pragma unroll
   for (int i = 0; i < kTK; ++i) {
     st.k[i][0] = *reinterpret_cast<const u32x4_t*>(g.kpages + row[i] + g.dc * 8);
-    st.k[i][1] = *reinterpret_cast<const u32x4_t*>(g.kpages + row[i] + 64 + g.dc * 8);
+    st.k[i][1] = *reinterpret_cast<const u32x4_t*>(g.kpages + row[i] + D / 2 + g.dc * 8);
   }
 #pragma unroll
   for (int i = 0; i < kTK; ++i) {
     st.v[i][0] = *reinterpret_cast<const u32x4_t*>(g.vpages + row[i] + g.dc * 8);
-    st.v[i][1] = *reinterpret_cast<const u32x4_t*>(g.vpages + row[i] + 64 + g.dc * 8);
+    st.v[i][1] = *reinterpret_cast<const u32x4_t*>(g.vpages + row[i] + D / 2 + g.dc * 8);
   }
 }
 
@@ -159,11 +169,12 @@ struct RowState {
   float acc[ROWS][16];
 };
 
-template <int ROWS>
+template <int ROWS, int D>
 __device__ __forceinline__ void compute_stage(const Stage& st, int t0, int s1, const uint32_t (&q)[ROWS][8],
                                               const int (&last)[ROWS], int min_last, float c, int kg,
                                               RowState<ROWS>& rs) {
-  // scores (raw q.k): lane-partial bf16 dot products, summed over the key's 8 lanes
+  constexpr int LPK = Geo<D>::LPK, KPI = Geo<D>::KPI, kStep = Geo<D>::kStep;
+  // scores (raw q.k): lane-partial bf16 dot products, summed over the key's LPK lanes
   float s[ROWS][kTK];
 #pragma unroll
   for (int i = 0; i < kTK; ++i) {
@@ -178,14 +189,14 @@ __device__ __forceinline__ void compute_stage(const Stage& st, int t0, int s1, c
       d = dot2_bf16(q[r][5], st.k[i][1].y, d);
       d = dot2_bf16(q[r][6], st.k[i][1].z, d);
       d = dot2_bf16(q[r][7], st.k[i][1].w, d);
-      s[r][i] = sum_lanes8(d);
+      s[r][i] = sum_lanes<LPK>(d);
     }
   }
   // visibility: past the split end, or hidden by the causal rule (separate from the load)
   if (t0 + kStep > s1 || t0 + kStep - 1 > min_last) {
 #pragma unroll
     for (int i = 0; i < kTK; ++i) {
-      const int key = t0 + kg + 8 * i;
+      const int key = t0 + kg + KPI * i;
 #pragma unroll
       for (int r = 0; r < ROWS; ++r)
         if (!(key < s1 && key <= last[r])) s[r][i] = -INFINITY;
@@ -198,7 +209,7 @@ __device__ __forceinline__ void compute_stage(const Stage& st, int t0, int s1, c
     float tmax = s[r][0];
 #pragma unroll
     for (int i = 1; i < kTK; ++i) tmax = fmaxf(tmax, s[r][i]);
-    tmax = max_stride8(tmax) * c;
+    tmax = max_stride<LPK>(tmax) * c;
     if (tmax > rs.m[r] + kTau) {  // uniform across the wave
       const float alpha = fast_exp2(rs.m[r] - tmax);  // 0 when the old reference is -inf
       rs.m[r] = tmax;
@@ -263,11 +274,10 @@ __device__ __forceinline__ int64_t seq_gran(const DecodeArgs& a, int b) {
   return seq_rows(a, b, start) > 0 ? n_gran(a.context_lens[b]) : 0;
 }
 
-// Element offset of query (and output) row l of head h of sequence b, which
-// has L rows starting at token `start`.
-__device__ __forceinline__ size_t row_off(const DecodeArgs& a, int b, int start, int L, int h, int l) {
-  return a.qstart ? ((size_t)(start + l) * a.num_q_heads + h) * 128
-                  : (((size_t)b * a.num_q_heads + h) * L + l) * 128;
+// Row index of query (and output) row l of head h of sequence b, which has
+// L rows starting at token `start` (rows are head_dim elements long).
+__device__ __forceinline__ size_t row_idx(const DecodeArgs& a, int b, int start, int L, int h, int l) {
+  return a.qstart ? (size_t)(start + l) * a.num_q_heads + h : ((size_t)b * a.num_q_heads + h) * L + l;
 }
 
 // Work item w covers granules [w * total / work_items, (w + 1) * total / work_items).
@@ -277,15 +287,16 @@ __device__ __forceinline__ int64_t gran_begin(int64_t w, int64_t total, int64_t 
 // rows of that kv head (sequence b has L rows from token `start`). Merges
 // the 4 waves' states and either stores the output (the piece is the whole
 // segment) or leaves the partial state in the workspace slot.
-template <int ROWS, bool ALIGNED>
+template <int ROWS, bool ALIGNED, int D>
 __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_bt, float (*lds_m)[ROWS],
-                                             float (*lds_l)[ROWS], float (*lds_acc)[ROWS][128], int b, int kvh,
+                                             float (*lds_l)[ROWS], float (*lds_acc)[ROWS][D], int b, int kvh,
                                              int ctx, int L, int start, int k0, int k1, bool direct, int slot) {
+  constexpr int LPK = Geo<D>::LPK, kStep = Geo<D>::kStep;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int kg = lane >> 3;
-  const int dc = lane & 7;
+  const int kg = lane / LPK;
+  const int dc = lane % LPK;
 
   // Query rows of this kv head: row r -> q head kvh*group + r / L, position r % L.
   const int rows = a.group * L;
@@ -296,9 +307,9 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
     if (r < rows) {
       const int h = kvh * a.group + r / L;
       const int l = r % L;
-      const uint16_t* qp = a.query + row_off(a, b, start, L, h, l);
+      const uint16_t* qp = a.query + row_idx(a, b, start, L, h, l) * D;
       const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(qp + dc * 8);
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(qp + 64 + dc * 8);
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(qp + D / 2 + dc * 8);
       q[r][0] = lo.x; q[r][1] = lo.y; q[r][2] = lo.z; q[r][3] = lo.w;
       q[r][4] = hi.x; q[r][5] = hi.y; q[r][6] = hi.z; q[r][7] = hi.w;
       last[r] = a.causal ? l + ctx - L : ctx - 1;
@@ -325,8 +336,8 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
   g.kpages = a.kpages;
   g.vpages = a.vpages;
   g.lds_bt = lds_bt;
-  g.page_stride = (size_t)a.page_size * 128 * a.num_kv_heads;
-  g.head_off = (size_t)kvh * a.page_size * 128;
+  g.page_stride = (size_t)a.page_size * D * a.num_kv_heads;
+  g.head_off = (size_t)kvh * a.page_size * D;
   g.page_size = a.page_size;
   g.ps_log2 = a.ps_log2;
   g.kg = kg;
@@ -356,13 +367,13 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
     if (t < kb) {
       Stage st[kStages];
 #pragma unroll
-      for (int i = 0; i < kStages - 1; ++i) load_stage<ALIGNED>(g, t + i * kStride, st[i]);
+      for (int i = 0; i < kStages - 1; ++i) load_stage<ALIGNED, D>(g, t + i * kStride, st[i]);
       bool done = false;
       while (!done) {
 #pragma unroll
         for (int j = 0; j < kStages; ++j) {
-          load_stage<ALIGNED>(g, t + (kStages - 1) * kStride, st[(j + kStages - 1) % kStages]);
-          compute_stage<ROWS>(st[j], t, kb, q, last, min_last, a.c, kg, rs);
+          load_stage<ALIGNED, D>(g, t + (kStages - 1) * kStride, st[(j + kStages - 1) % kStages]);
+          compute_stage<ROWS, D>(st[j], t, kb, q, last, min_last, a.c, kg, rs);
           t += kStride;
           if (t >= kb) {
             done = true;
@@ -376,9 +387,9 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
   // ---- merge: lanes of the wave (same reference), then the 4 waves in LDS ----
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    rs.lsum[r] = sum_stride8(rs.lsum[r]);  // over the 8 key groups of the wave
+    rs.lsum[r] = sum_stride<LPK>(rs.lsum[r]);  // over the key groups of the wave
 #pragma unroll
-    for (int j = 0; j < 16; ++j) rs.acc[r][j] = sum_stride8(rs.acc[r][j]);
+    for (int j = 0; j < 16; ++j) rs.acc[r][j] = sum_stride<LPK>(rs.acc[r][j]);
   }
   if (kg == 0) {
 #pragma unroll
@@ -386,7 +397,7 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         lds_acc[wave][r][dc * 8 + j] = rs.acc[r][j];
-        lds_acc[wave][r][64 + dc * 8 + j] = rs.acc[r][8 + j];
+        lds_acc[wave][r][D / 2 + dc * 8 + j] = rs.acc[r][8 + j];
       }
     }
     if (dc == 0) {
@@ -399,9 +410,9 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
   }
   __syncthreads();
   const size_t part = ((size_t)blockIdx.x * 2 + slot) * a.rows;
-  for (int idx = tid; idx < rows * 128; idx += kThreads) {
-    const int r = idx >> 7;
-    const int d = idx & 127;
+  for (int idx = tid; idx < rows * D; idx += kThreads) {
+    const int r = idx / D;
+    const int d = idx % D;
     float mw[kWaves];
     float M = -INFINITY;
 #pragma unroll
@@ -419,10 +430,10 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
     if (direct) {
       const int h = kvh * a.group + r / L;
       const int l = r % L;
-      a.out[row_off(a, b, start, L, h, l) + d] = to_bf16(num / den);
+      a.out[row_idx(a, b, start, L, h, l) * D + d] = to_bf16(num / den);
     } else {
       // device-coherent stores (no cache-wide fence needed; see arrive_last)
-      store_coherent(a.ws_acc + (part + r) * 128 + d, num);
+      store_coherent(a.ws_acc + (part + r) * D + d, num);
       if (d == 0) {
         store_coherent(a.ws_ml + (part + r) * 2 + 0, M);
         store_coherent(a.ws_ml + (part + r) * 2 + 1, den);
@@ -474,12 +485,13 @@ __device__ __forceinline__ SegmentItems segment_items(int64_t S, int64_t E, int6
 // dimensions in parallel). Work item w's piece sits in slot 0 when the
 // segment is the first piece of w's range, else in slot 1. Partials with
 // maximum -inf (no visible key) contribute 0.
+template <int D>
 __device__ void merge_segment(const DecodeArgs& a, int b, int kvh, int L, int start, int64_t S,
                               const SegmentItems& it, int64_t total) {
   const int64_t P = a.work_items;
-  for (int idx = threadIdx.x; idx < a.group * L * 128; idx += kThreads) {
-    const int r = idx >> 7;
-    const int d = idx & 127;
+  for (int idx = threadIdx.x; idx < a.group * L * D; idx += kThreads) {
+    const int r = idx / D;
+    const int d = idx % D;
     float M = -INFINITY;
     for (int64_t w = it.wf; w <= it.wl; ++w) {
       const int64_t gw = gran_begin(w, total, P);
@@ -495,20 +507,20 @@ __device__ void merge_segment(const DecodeArgs& a, int b, int kvh, int L, int st
       const float mj = load_coherent(a.ws_ml + part * 2);
       const float f = mj == -INFINITY ? 0.f : fast_exp2(mj - M);
       den = fmaf(f, load_coherent(a.ws_ml + part * 2 + 1), den);
-      num = fmaf(f, load_coherent(a.ws_acc + part * 128 + d), num);
+      num = fmaf(f, load_coherent(a.ws_acc + part * D + d), num);
     }
     const int h = kvh * a.group + r / L;
     const int l = r % L;
-    a.out[row_off(a, b, start, L, h, l) + d] = to_bf16(num / den);
+    a.out[row_idx(a, b, start, L, h, l) * D + d] = to_bf16(num / den);
   }
 }
 
-template <int ROWS, bool ALIGNED>
+template <int ROWS, bool ALIGNED, int D>
 __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
   extern __shared__ int32_t lds_bt[];
   __shared__ float lds_m[kWaves][ROWS];
   __shared__ float lds_l[kWaves][ROWS];
-  __shared__ float lds_acc[kWaves][ROWS][128];
+  __shared__ float lds_acc[kWaves][ROWS][D];
   __shared__ int64_t lds_scan[kThreads];
   __shared__ int64_t lds_start[2];  // (sequence holding the first granule, its granule prefix)
   __shared__ bool lds_last;
@@ -568,8 +580,8 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
     const int k0 = (int)((G - S) * kGran);
     const int k1 = (int)min((gend - S) * kGran, (int64_t)ctx);
     const bool direct = G == S && gend == E;
-    decode_piece<ROWS, ALIGNED>(a, lds_bt, lds_m, lds_l, lds_acc, b, kvh, ctx, L, start, k0, k1, direct,
-                                nth == 0 ? 0 : 1);
+    decode_piece<ROWS, ALIGNED, D>(a, lds_bt, lds_m, lds_l, lds_acc, b, kvh, ctx, L, start, k0, k1, direct,
+                                   nth == 0 ? 0 : 1);
     if (!direct) {
       // publish this piece, then the last of the segment's work items merges it
       wait_stores();
@@ -577,7 +589,7 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
       const SegmentItems it = segment_items(S, E, total, a.work_items);
       if (tid == 0) lds_last = arrive_last(a.ws_ctr + (size_t)b * a.num_kv_heads + kvh, a.epoch, it.count);
       __syncthreads();
-      if (lds_last) merge_segment(a, b, kvh, L, start, S, it, total);
+      if (lds_last) merge_segment<D>(a, b, kvh, L, start, S, it, total);
     }
     G = gend;
     ++nth;
@@ -588,15 +600,16 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
   }
 }
 
-template <int ROWS, bool ALIGNED>
+template <int ROWS, bool ALIGNED, int D>
 hipError_t launch_work(const DecodeArgs& a, size_t lds_bytes, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_decode_work<ROWS, ALIGNED>), dim3((unsigned)a.work_items), dim3(kThreads), lds_bytes,
+  hipLaunchKernelGGL((pa_decode_work<ROWS, ALIGNED, D>), dim3((unsigned)a.work_items), dim3(kThreads), lds_bytes,
                      stream, a);
   return hipGetLastError();
 }
 
-// Work items the GPU keeps resident for one kernel instance (cached per device).
-template <int ROWS, bool ALIGNED>
+// Work items the GPU keeps resident for one kernel instance (cached per
+// device; registers, not shared memory, bound it for every page size).
+template <int ROWS, bool ALIGNED, int D>
 int resident_items(size_t lds_bytes) {
   static int cache[64] = {0};
   int dev = 0;
@@ -604,7 +617,7 @@ int resident_items(size_t lds_bytes) {
   if (cache[dev] > 0) return cache[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)pa_decode_work<ROWS, ALIGNED>, kThreads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)pa_decode_work<ROWS, ALIGNED, D>, kThreads,
                                                    lds_bytes) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   const int n = cus * per_cu;
@@ -612,14 +625,24 @@ int resident_items(size_t lds_bytes) {
   return n;
 }
 
-template <int ROWS>
+template <int ROWS, int D>
 hipError_t launch_rows(DecodeArgs& a, bool aligned, int requested, int cap, size_t lds, hipStream_t st) {
   if (aligned) {
-    a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, true>(lds));
-    return launch_work<ROWS, true>(a, lds, st);
+    a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, true, D>(lds));
+    return launch_work<ROWS, true, D>(a, lds, st);
   }
-  a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, false>(lds));
-  return launch_work<ROWS, false>(a, lds, st);
+  a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, false, D>(lds));
+  return launch_work<ROWS, false, D>(a, lds, st);
+}
+
+template <int D>
+hipError_t launch_dim(DecodeArgs& a, const Plan& p, size_t lds, hipStream_t stream) {
+  switch (p.rows_pad) {
+    case 1: return launch_rows<1, D>(a, p.aligned, p.work_items, p.work_cap, lds, stream);
+    case 2: return launch_rows<2, D>(a, p.aligned, p.work_items, p.work_cap, lds, stream);
+    case 4: return launch_rows<4, D>(a, p.aligned, p.work_items, p.work_cap, lds, stream);
+    default: return launch_rows<8, D>(a, p.aligned, p.work_items, p.work_cap, lds, stream);
+  }
 }
 
 }  // namespace
@@ -652,14 +675,11 @@ hipError_t launch_decode(const KernelArgs& k, const Plan& p, hipStream_t stream)
   a.total_query = k.total_query;
   if (k.query_start) a.query_len = k.dec_max_len;  // the longest query this launch serves
   const size_t lds = (size_t)p.bt_entries * sizeof(int32_t);
-  hipError_t e;
-  switch (p.rows_pad) {
-    case 1: e = launch_rows<1>(a, p.aligned, p.work_items, p.work_cap, lds, stream); break;
-    case 2: e = launch_rows<2>(a, p.aligned, p.work_items, p.work_cap, lds, stream); break;
-    case 4: e = launch_rows<4>(a, p.aligned, p.work_items, p.work_cap, lds, stream); break;
-    default: e = launch_rows<8>(a, p.aligned, p.work_items, p.work_cap, lds, stream); break;
+  switch (k.head_dim) {
+    case 64: return launch_dim<64>(a, p, lds, stream);
+    case 256: return launch_dim<256>(a, p, lds, stream);
+    default: return launch_dim<128>(a, p, lds, stream);
   }
-  return e;
 }
 
 }  // namespace pa

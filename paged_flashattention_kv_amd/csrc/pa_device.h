@@ -44,6 +44,7 @@ enum : int {
   kDppQuadXor2 = 0x4E,       // quad_perm [2,3,0,1]
   kDppRowHalfMirror = 0x141,  // lane i <-> 7 - i inside each half row
   kDppRowMirror = 0x140,      // lane i <-> 15 - i inside each row
+  kDppRowRor4 = 0x124,        // rotate right by 4 inside each row
   kDppRowRor8 = 0x128,        // rotate right by 8 inside each row (= xor 8)
 };
 
@@ -52,26 +53,36 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, false));
 }
 
-// Sum over the 8 consecutive lanes of an aligned group of 8; every lane of
-// the group receives the total.
-__device__ __forceinline__ float sum_lanes8(float x) {
+// Sum over the N consecutive lanes of an aligned group of N (N = 4, 8 or
+// 16); every lane of the group receives the total.
+template <int N>
+__device__ __forceinline__ float sum_lanes(float x) {
+  static_assert(N == 4 || N == 8 || N == 16, "groups of 4, 8 or 16 lanes");
   x += dpp<kDppQuadXor1>(x);
   x += dpp<kDppQuadXor2>(x);
-  x += dpp<kDppRowHalfMirror>(x);
+  if (N >= 8) x += dpp<kDppRowHalfMirror>(x);
+  if (N >= 16) x += dpp<kDppRowMirror>(x);
   return x;
 }
 
-// Reductions over lanes {i, i^8, i^16, ..., i^56}: the eight lanes that share
-// (lane % 8). xor 8 stays inside a DPP row; xor 16 and 32 cross rows.
-__device__ __forceinline__ float max_stride8(float x) {
-  x = fmaxf(x, dpp<kDppRowRor8>(x));
+// Reductions over the lanes that share (lane % S) (S = 4, 8 or 16): the orbit
+// of lane i under rotations by S inside its 16-lane DPP row, then xor 16 and
+// 32 across rows.
+template <int S>
+__device__ __forceinline__ float max_stride(float x) {
+  static_assert(S == 4 || S == 8 || S == 16, "strides of 4, 8 or 16 lanes");
+  if (S == 4) x = fmaxf(x, dpp<kDppRowRor4>(x));
+  if (S <= 8) x = fmaxf(x, dpp<kDppRowRor8>(x));
   x = fmaxf(x, __shfl_xor(x, 16));
   x = fmaxf(x, __shfl_xor(x, 32));
   return x;
 }
 
-__device__ __forceinline__ float sum_stride8(float x) {
-  x += dpp<kDppRowRor8>(x);
+template <int S>
+__device__ __forceinline__ float sum_stride(float x) {
+  static_assert(S == 4 || S == 8 || S == 16, "strides of 4, 8 or 16 lanes");
+  if (S == 4) x += dpp<kDppRowRor4>(x);
+  if (S <= 8) x += dpp<kDppRowRor8>(x);
   x += __shfl_xor(x, 16);
   x += __shfl_xor(x, 32);
   return x;

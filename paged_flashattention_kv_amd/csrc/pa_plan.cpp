@@ -34,7 +34,8 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
   if (check_pool && s.num_pages < 1) return fail(err, kErrInvalid, "num_pages must be positive");
   if (s.num_q_heads % s.num_kv_heads != 0)
     return fail(err, kErrInvalid, "num_q_heads must be a multiple of num_kv_heads");
-  if (s.head_dim != kHeadDim) return fail(err, kErrUnsupported, "only head_dim == 128 is implemented");
+  if (!head_dim_supported(s.head_dim))
+    return fail(err, kErrUnsupported, "head_dim must be 64, 128 or 256");
   const int64_t max_ctx = s.max_pages * s.page_size;
   if (max_ctx > INT32_MAX) return fail(err, kErrUnsupported, "max_pages * page_size exceeds int32");
   if (s.causal && max_ctx < s.query_len)
@@ -67,13 +68,13 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
     if (granules > (int64_t(1) << 62) / p.work_cap)
       return fail(err, kErrUnsupported, "decode work too large for the granule arithmetic");
     p.bt_entries = int(kDecodeWindow / s.page_size + 2);
-    p.aligned = s.page_size % kDecodeStep == 0;  // a wave step lies inside one page
+    p.aligned = s.page_size % decode_step(s.head_dim) == 0;  // a wave step lies inside one page
     p.num_work = p.work_cap;
     const size_t slots = size_t(p.work_cap) * 2 * size_t(p.rows);
     p.ws_ctr_offset = 0;
     p.ws_ml_offset = align_up(size_t(s.batch) * size_t(s.num_kv_heads) * sizeof(uint64_t), 256);
     p.ws_acc_offset = align_up(p.ws_ml_offset + slots * 2 * sizeof(float), 256);
-    p.workspace_bytes = align_up(p.ws_acc_offset + slots * kHeadDim * sizeof(float), 256);
+    p.workspace_bytes = align_up(p.ws_acc_offset + slots * size_t(s.head_dim) * sizeof(float), 256);
   } else {
     p.n_qtiles = int(cdiv(s.query_len, kPrefillBlockM));
     p.aligned = s.page_size % kPrefillBlockN == 0;

@@ -11,8 +11,10 @@
 
 namespace pa {
 
-constexpr int kHeadDim = 128;        // the only head_dim the kernels implement
-constexpr int kDecodeStep = 16;      // keys per decode wave step
+// head dims the kernels implement
+constexpr bool head_dim_supported(int64_t d) { return d == 64 || d == 128 || d == 256; }
+// keys per decode wave step: 8 KB of K and V (two keys per lane, 16 dims each)
+constexpr int decode_step(int64_t head_dim) { return int(2048 / head_dim); }
 constexpr int kDecodeMaxRows = 8;    // q rows (GQA group x query_len) per decode work item
 constexpr int kDecodeWindow = 2048;  // keys whose block-table entries a decode work item stages at once
 constexpr int kDecodeAutoCap = 2048; // most decode work items the automatic choice launches

@@ -30,9 +30,12 @@
 // Page-translating loader ("Week 3 Day 5", Task 1): each K/V tile is
 // resolved through block_table while it is staged, straight from HBM into
 // LDS (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l). A
-// wave instruction moves 4 key rows of 256 bytes. Rows are stored with their
-// 16-byte chunks XOR-swizzled by the key index so that both the K fragment
-// reads and the V transposed reads spread over all LDS banks. Aligned path
+// wave instruction moves 1 KiB: 4 key rows of 256 bytes at head dim 128 (8
+// rows at 64, 2 at 256). Rows are stored with their 16-byte chunks
+// XOR-swizzled by the key index so that both the K fragment reads and the V
+// transposed reads spread over the LDS banks. Head dims 64, 128 and 256 share
+// the code: D/16 contraction steps for Q K^T, D/32 output blocks for P V; at
+// 256 the four tile buffers take 128 KiB of LDS and one work item runs per CU. Aligned path
 // (page_size % 64 == 0): the tile is one contiguous span of one page, found
 // with a single table entry. Generic path: each key row is translated on
 // its own (tiles that cross pages). Keys at or past the context end read a
@@ -54,7 +57,22 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBM = kPrefillBlockM;       // 128 query rows
 constexpr int kBN = kPrefillBlockN;       // 64 keys
-constexpr int kTileBytes = kBN * 256;     // one K (or V) tile in LDS: 16 KiB
+
+// Geometry for head dim D (64, 128 or 256): a key row is 2D bytes = D/8
+// chunks of 16 bytes; one global_load_lds instruction (64 lanes x 16 bytes)
+// moves 1024 / (2D) rows, and a wave stages its 16 rows of a tile in D/32
+// instructions.
+template <int D>
+struct Tile {
+  static_assert(D == 64 || D == 128 || D == 256, "head dims 64, 128 and 256");
+  static constexpr int kBytes = kBN * 2 * D;  // one K (or V) tile in LDS
+  static constexpr int kChunks = D / 8;       // 16-byte chunks per key row
+  static constexpr int kRowsPerInst = 512 / D;
+  static constexpr int kInsts = D / 32;       // load instructions per wave per tile
+  static constexpr int kKs = D / 16;          // 16-dim contraction steps of S = Q K^T
+  static constexpr int kDb = D / 32;          // 32-dim output blocks of O = P V
+  static constexpr int kBlocksPerCU = D <= 128 ? 2 : 1;  // LDS: 4 tiles per work item
+};
 // The exponent reference of a row moves only when a tile maximum exceeds it
 // by more than kTau (log2 units), so weights stay <= 2^kTau.
 constexpr float kTau = 8.0f;
@@ -83,62 +101,77 @@ struct PrefillArgs {
 
 __device__ __forceinline__ int div_ps(int s, int ps, int ps_log2) { return ps_log2 >= 0 ? (s >> ps_log2) : s / ps; }
 
-// 16-byte chunk c of key row `key` sits at chunk position c ^ swz(key).
-__device__ __forceinline__ int swz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
+// 16-byte chunk c of key row `key` sits at chunk position c ^ swz(key). The
+// swizzle spreads the K fragment reads (32 keys, one chunk each) and the
+// transposed V reads over the LDS banks. 256-byte rows (D = 128) and longer
+// ones take a 4-bit swizzle of the low chunk bits; 128-byte rows (D = 64),
+// two to a bank line, a bit-reversed 3-bit index of the key pair.
+template <int D>
+__device__ __forceinline__ int swz(int key) {
+  if (D == 64) {
+    const int j = (key >> 1) & 7;
+    return ((j & 1) << 2) | (j & 2) | ((j >> 2) & 1);
+  }
+  return ((key & 7) << 1) | ((key >> 3) & 1);
+}
 
 // Byte offset of (key, chunk) inside a tile buffer.
-__device__ __forceinline__ int tile_off(int key, int chunk) { return key * 256 + ((chunk ^ swz(key)) << 4); }
+template <int D>
+__device__ __forceinline__ int tile_off(int key, int chunk) { return key * (2 * D) + ((chunk ^ swz<D>(key)) << 4); }
 
 // Page lookup for the next tile to stage: the element offset of the key row
 // each of the lane's 4 load instructions reads (generic path), or the
 // tile's base row (aligned path, one entry).
-template <bool ALIGNED>
+template <bool ALIGNED, int D>
 struct TilePages {
-  size_t row[ALIGNED ? 1 : 4];
+  size_t row[ALIGNED ? 1 : Tile<D>::kInsts];
 };
 
 typedef __attribute__((address_space(4))) const int32_t constant_i32;
 
-template <bool ALIGNED>
+template <bool ALIGNED, int D>
 __device__ __forceinline__ void lookup_tile(const PrefillArgs& a, const int32_t* bt_row, size_t page_stride,
                                             size_t head_off, int ctx, int t0, int wave, int lane,
-                                            TilePages<ALIGNED>& tp) {
+                                            TilePages<ALIGNED, D>& tp) {
+  using T = Tile<D>;
   if (ALIGNED) {
     // one uniform entry per tile: a scalar load (the table is read-only here)
     const int lp = div_ps(t0, a.page_size, a.ps_log2);
     const int32_t page = ((constant_i32*)bt_row)[lp];
-    tp.row[0] = (size_t)page * page_stride + head_off + (size_t)(t0 - lp * a.page_size) * 128;
+    tp.row[0] = (size_t)page * page_stride + head_off + (size_t)(t0 - lp * a.page_size) * D;
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int key = t0 + 4 * (4 * wave + i) + (lane >> 4);
+    for (int i = 0; i < T::kInsts; ++i) {
+      int key = t0 + 16 * wave + T::kRowsPerInst * i + lane / T::kChunks;
       key = key < ctx ? key : ctx - 1;  // past the context: re-read a valid row
       const int lp = div_ps(key, a.page_size, a.ps_log2);
-      tp.row[i] = (size_t)bt_row[lp] * page_stride + head_off + (size_t)(key - lp * a.page_size) * 128;
+      tp.row[i] = (size_t)bt_row[lp] * page_stride + head_off + (size_t)(key - lp * a.page_size) * D;
     }
   }
 }
 
 // Issues the direct HBM -> LDS loads of one K/V tile. Wave w moves keys
-// [16w, 16w + 16) of the tile: instruction i covers keys 4(4w+i) .. +3, lane
-// l key 4(4w+i) + l/16 and LDS chunk position l % 16, which holds global
-// chunk (l % 16) ^ swz(key).
-template <bool ALIGNED>
-__device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages<ALIGNED>& tp, int ctx, int t0,
+// [16w, 16w + 16) of the tile: instruction i covers the kRowsPerInst keys
+// from 16w + kRowsPerInst*i; lane l takes key 16w + kRowsPerInst*i + l/kChunks
+// and LDS chunk position l % kChunks, which holds global chunk
+// (l % kChunks) ^ swz(key).
+template <bool ALIGNED, int D>
+__device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages<ALIGNED, D>& tp, int ctx, int t0,
                                            int wave, int lane, char* kbuf, char* vbuf) {
+  using T = Tile<D>;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int key = 4 * (4 * wave + i) + (lane >> 4);  // key inside the tile
-    const int chunk = (lane & 15) ^ swz(key);
+  for (int i = 0; i < T::kInsts; ++i) {
+    const int key = 16 * wave + T::kRowsPerInst * i + lane / T::kChunks;  // key inside the tile
+    const int chunk = (lane % T::kChunks) ^ swz<D>(key);
     size_t row;
     if (ALIGNED) {
       // the tile lies in one page; keys past the context re-read the tile's first row
-      row = tp.row[0] + (size_t)(t0 + key < ctx ? key : 0) * 128;
+      row = tp.row[0] + (size_t)(t0 + key < ctx ? key : 0) * D;
     } else {
       row = tp.row[i];
     }
     const size_t off = row + (size_t)chunk * 8;
-    const int lds_off = (4 * wave + i) * 1024;
+    const int lds_off = wave * 32 * D + i * 1024;
     __builtin_amdgcn_global_load_lds((global_void*)(a.kpages + off), (lds_void*)(kbuf + lds_off), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((global_void*)(a.vpages + off), (lds_void*)(vbuf + lds_off), 16, 0, 0);
   }
@@ -146,12 +179,13 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages
 
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <bool ALIGNED>
-__global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds_k0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_k1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_v0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_v1[kTileBytes];
+template <bool ALIGNED, int D>
+__global__ void __launch_bounds__(kThreads, Tile<D>::kBlocksPerCU) pa_prefill_mfma(PrefillArgs a) {
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) char lds_k0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -197,37 +231,37 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
   const int wave_last_row = min(r0 + 31, L - 1);
   const int wave_kv_end = a.causal ? min(ctx, wave_last_row + offset + 1) : ctx;
 
-  const size_t head_stride = (size_t)a.page_size * 128;
+  const size_t head_stride = (size_t)a.page_size * D;
   const size_t page_stride = head_stride * a.num_kv_heads;
   const size_t head_off = (size_t)kvh * head_stride;
   const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
 
   // ---- first tile in flight before anything else ----
-  TilePages<ALIGNED> tp;
+  TilePages<ALIGNED, D> tp;
   if (n_tiles > 0) {
-    lookup_tile<ALIGNED>(a, bt_row, page_stride, head_off, ctx, 0, wave, lane, tp);
-    issue_tile<ALIGNED>(a, tp, ctx, 0, wave, lane, lds_k0, lds_v0);
-    lookup_tile<ALIGNED>(a, bt_row, page_stride, head_off, ctx, min(1, n_tiles - 1) * kBN, wave, lane, tp);
+    lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, 0, wave, lane, tp);
+    issue_tile<ALIGNED, D>(a, tp, ctx, 0, wave, lane, lds_k0, lds_v0);
+    lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, min(1, n_tiles - 1) * kBN, wave, lane, tp);
   }
 
   // ---- Q^T operand: lane holds row r0 + col, dims 16ks + 8half .. +8 ----
-  bf16x8_t qv[8];
+  bf16x8_t qv[T::kKs];
   {
     const int row = r0 + col;
     const int rr = row < L ? row : 0;
     const size_t qrow = a.qstart ? (size_t)(start + rr) * a.num_q_heads + head : ((size_t)b * a.num_q_heads + head) * L + rr;
-    const uint16_t* qp = a.query + qrow * 128 + 8 * half;
+    const uint16_t* qp = a.query + qrow * D + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < T::kKs; ++ks) {
       u32x4_t w = u32x4_t{0u, 0u, 0u, 0u};
       if (row < L) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
       qv[ks] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
 
-  f32x16_t acc_o[4];
+  f32x16_t acc_o[T::kDb];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < T::kDb; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;
   float m_run = -INFINITY;
@@ -252,9 +286,9 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
     const int t0 = t * kBN;
     wait_all_loads();  // this wave's part of tile t (and the next lookup) has landed
     __syncthreads();   // every wave's part is in LDS; every wave is done with tile t - 1
-    if (t + 1 < n_tiles) issue_tile<ALIGNED>(a, tp, ctx, t0 + kBN, wave, lane, knext, vnext);
+    if (t + 1 < n_tiles) issue_tile<ALIGNED, D>(a, tp, ctx, t0 + kBN, wave, lane, knext, vnext);
     // lookup for tile t + 2 (clamped so that it is unconditional)
-    lookup_tile<ALIGNED>(a, bt_row, page_stride, head_off, ctx, min(t + 2, n_tiles - 1) * kBN, wave, lane, tp);
+    lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, min(t + 2, n_tiles - 1) * kBN, wave, lane, tp);
     if (!wave_has_rows || t0 >= wave_kv_end) return;
 
       // ---- S^T = K Q^T : two 32-key blocks ----
@@ -265,9 +299,9 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
         for (int i = 0; i < 16; ++i) acc_s[kb][i] = 0.f;
         const int key = 32 * kb + col;
   #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8_t kfrag =
-              __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(kb_base + tile_off(key, 2 * ks + half)));
+        for (int ks = 0; ks < T::kKs; ++ks) {
+          const bf16x8_t kfrag = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(kb_base + tile_off<D>(key, 2 * ks + half)));
           acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qv[ks], acc_s[kb], 0, 0, 0);
         }
       }
@@ -308,7 +342,7 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
         m_run = grow ? tmax : m_run;
         l_run *= alpha;
   #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < T::kDb; ++db)
   #pragma unroll
           for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
       }
@@ -335,12 +369,12 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
         const bf16x8_t pfrag = __builtin_bit_cast(bf16x8_t, pw);
         const int key0 = 16 * ks + vk_lane;
   #pragma unroll
-        for (int db = 0; db < 4; ++db) {
+        for (int db = 0; db < T::kDb; ++db) {
           const int c = 4 * db + vc_lane;
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(vb_base + tile_off(key0, c) + vb_lane));
+              (__attribute__((address_space(3))) i16x4_t*)(vb_base + tile_off<D>(key0, c) + vb_lane));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(vb_base + tile_off(key0 + 8, c) + vb_lane));
+              (__attribute__((address_space(3))) i16x4_t*)(vb_base + tile_off<D>(key0 + 8, c) + vb_lane));
           const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
           const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
           const u32x4_t vw = {lw.x, lw.y, hw.x, hw.y};
@@ -361,9 +395,9 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
   const float inv = 1.f / l_tot;
   const size_t orow = a.qstart ? (size_t)(start + row_abs) * a.num_q_heads + head
                                : ((size_t)b * a.num_q_heads + head) * L + row_abs;
-  uint16_t* op = a.out + orow * 128;
+  uint16_t* op = a.out + orow * D;
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < T::kDb; ++db) {
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
       const int d0 = 32 * db + 8 * grp + 4 * half;
@@ -372,6 +406,15 @@ __global__ void __launch_bounds__(kThreads, 2) pa_prefill_mfma(PrefillArgs a) {
       *reinterpret_cast<u32x2_t*>(op + d0) = w;
     }
   }
+}
+
+template <int D>
+hipError_t launch_dim(const PrefillArgs& a, const Plan& p, hipStream_t stream) {
+  if (p.aligned)
+    hipLaunchKernelGGL((pa_prefill_mfma<true, D>), dim3((unsigned)p.num_work), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((pa_prefill_mfma<false, D>), dim3((unsigned)p.num_work), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -398,11 +441,11 @@ hipError_t launch_prefill(const KernelArgs& k, const Plan& p, hipStream_t stream
   a.qstart = k.query_start;
   a.total_query = k.total_query;
   a.skip_len = k.query_start ? k.dec_max_len : 0;
-  if (p.aligned)
-    hipLaunchKernelGGL(pa_prefill_mfma<true>, dim3((unsigned)p.num_work), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(pa_prefill_mfma<false>, dim3((unsigned)p.num_work), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  switch (k.head_dim) {
+    case 64: return launch_dim<64>(a, p, stream);
+    case 256: return launch_dim<256>(a, p, stream);
+    default: return launch_dim<128>(a, p, stream);
+  }
 }
 
 }  // namespace pa

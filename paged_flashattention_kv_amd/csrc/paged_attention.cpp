@@ -99,6 +99,7 @@ int paged_attention_ex(const void* query, const void* key_pages, const void* val
   k.num_pages = num_pages;
   k.page_size = page_size;
   k.max_pages = max_pages;
+  k.head_dim = head_dim;
   k.scale = scale;
   k.causal = causal;
   k.epoch = next_epoch();
@@ -200,12 +201,12 @@ int paged_kv_append(const void* key_new, const void* value_new, void* key_pages,
   if (batch < 1 || num_kv_heads < 1 || new_len < 1 || head_dim < 1 || num_pages < 1 || page_size < 1 ||
       max_pages < 1)
     return set_error(PA_ERR_INVALID, "all sizes must be positive");
-  if (head_dim != pa::kHeadDim) return set_error(PA_ERR_UNSUPPORTED, "only head_dim == 128 is implemented");
+  if (!pa::head_dim_supported(head_dim)) return set_error(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
   const int64_t max_ctx = int64_t(max_pages) * page_size;
   if (max_ctx > INT32_MAX) return set_error(PA_ERR_UNSUPPORTED, "max_pages * page_size exceeds int32");
   if (max_ctx < new_len) return set_error(PA_ERR_INVALID, "max_pages * page_size < new_len");
   const int64_t rows = int64_t(batch) * num_kv_heads * new_len;
-  if (rows > (int64_t(1) << 35)) return set_error(PA_ERR_UNSUPPORTED, "batch * num_kv_heads * new_len too large");
+  if (rows > (int64_t(1) << 34)) return set_error(PA_ERR_UNSUPPORTED, "batch * num_kv_heads * new_len too large");
   const size_t new_bytes = size_t(rows) * head_dim * 2;
   const size_t pool_bytes = size_t(num_pages) * num_kv_heads * page_size * head_dim * 2;
   if (overlaps(key_pages, pool_bytes, value_pages, pool_bytes))
@@ -226,6 +227,7 @@ int paged_kv_append(const void* key_new, const void* value_new, void* key_pages,
   k.num_pages = num_pages;
   k.page_size = page_size;
   k.max_pages = max_pages;
+  k.head_dim = head_dim;
   const hipError_t e = pa::launch_append(k, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, std::string("launch failed: ") + hipGetErrorString(e));
   g_last_error.clear();
@@ -287,6 +289,7 @@ int paged_attention_varlen_ex(const void* query, const void* key_pages, const vo
   k.num_pages = num_pages;
   k.page_size = page_size;
   k.max_pages = max_pages;
+  k.head_dim = head_dim;
   k.scale = scale;
   k.causal = causal;
   k.epoch = next_epoch();

@@ -28,7 +28,19 @@ int main() {
   // invalid sizes
   CHECK(pa::make_plan(shape(0, 32, 8, 1, 128, 16, 4), 0, 0, true, &p, &err) == pa::kErrInvalid);
   CHECK(pa::make_plan(shape(1, 30, 8, 1, 128, 16, 4), 0, 0, true, &p, &err) == pa::kErrInvalid);
-  CHECK(pa::make_plan(shape(1, 32, 8, 1, 64, 16, 4), 0, 0, true, &p, &err) == pa::kErrUnsupported);
+  CHECK(pa::make_plan(shape(1, 32, 8, 1, 96, 16, 4), 0, 0, true, &p, &err) == pa::kErrUnsupported);
+  CHECK(pa::make_plan(shape(1, 32, 8, 1, 512, 16, 4), 0, 0, true, &p, &err) == pa::kErrUnsupported);
+  // other head dims: the decode step (8 KB of K and V per wave) and the workspace follow D
+  for (int D : {64, 128, 256}) {
+    for (int ps : {8, 16, 32, 64, 5}) {
+      CHECK(pa::make_plan(shape(2, 8, 2, 1, D, ps, 40), 0, 0, true, &p, &err) == pa::kOk);
+      CHECK(p.schedule == pa::kScheduleDecode && p.aligned == (ps % (2048 / D) == 0));
+    }
+    CHECK(pa::make_plan(shape(2, 8, 2, 1, D, 16, 40), 0, 0, true, &p, &err) == pa::kOk);
+    CHECK(p.workspace_bytes >= size_t(p.work_cap) * 2 * 4 * D * 4);
+    CHECK(pa::make_plan(shape(2, 8, 2, 100, D, 64, 40), 0, 0, true, &p, &err) == pa::kOk);
+    CHECK(p.schedule == pa::kSchedulePrefill && p.aligned);
+  }
   CHECK(pa::make_plan(shape(1, 32, 8, 100, 128, 16, 4), 0, 0, true, &p, &err) == pa::kErrInvalid);
   CHECK(pa::make_plan(shape(1, 32, 8, 100, 128, 16, 4, false), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(pa::make_plan(shape(1, 32, 8, 1, 128, 16, 4), 3, 0, true, &p, &err) == pa::kErrInvalid);
@@ -70,7 +82,7 @@ int main() {
     CHECK(pa::make_plan(shape(2, 8, 8, 1, 128, ps, 10), 1, 0, true, &p, &err) == pa::kOk);
     const int worst = (pa::kDecodeWindow - 1 + ps - 1) / ps + 1;  // window starting one key into a page
     CHECK(p.bt_entries >= worst);
-    CHECK(p.aligned == (ps % pa::kDecodeStep == 0));
+    CHECK(p.aligned == (ps % pa::decode_step(128) == 0));
   }
   // explicit work item counts size the workspace
   CHECK(pa::make_plan(shape(2, 8, 8, 1, 128, 16, 10), 1, 7, true, &p, &err) == pa::kOk);

@@ -62,7 +62,9 @@ def _call(lib, **kw):
         (dict(L=200), native.PA_ERR_INVALID),
         (dict(causal=2), native.PA_ERR_INVALID),
         (dict(scale=float("nan")), native.PA_ERR_INVALID),
-        (dict(D=64), native.PA_ERR_UNSUPPORTED),
+        (dict(D=96), native.PA_ERR_UNSUPPORTED),
+        (dict(D=512), native.PA_ERR_UNSUPPORTED),
+        (dict(D=0), native.PA_ERR_INVALID),
         (dict(sched=7), native.PA_ERR_INVALID),
         (dict(L=5, sched=1), native.PA_ERR_INVALID),  # 10 rows > 8
         (dict(sched=1, split=-1), native.PA_ERR_INVALID),
@@ -94,7 +96,7 @@ def _append(lib, **kw):
         (dict(B=0), native.PA_ERR_INVALID),
         (dict(L=0), native.PA_ERR_INVALID),
         (dict(ps=0), native.PA_ERR_INVALID),
-        (dict(D=64), native.PA_ERR_UNSUPPORTED),
+        (dict(D=96), native.PA_ERR_UNSUPPORTED),
         (dict(L=65, ps=16, mp=4), native.PA_ERR_INVALID),  # 65 new tokens cannot fit 4 pages of 16
         (dict(mp=1 << 20, ps=1 << 12), native.PA_ERR_UNSUPPORTED),  # positions past int32
         (dict(vp=FAKE + 0x200000 + 4096), native.PA_ERR_INVALID),  # the two pools overlap
@@ -129,7 +131,7 @@ def _varlen(lib, **kw):
         (dict(Hq=3), native.PA_ERR_INVALID),
         (dict(causal=2), native.PA_ERR_INVALID),
         (dict(scale=float("inf")), native.PA_ERR_INVALID),
-        (dict(D=64), native.PA_ERR_UNSUPPORTED),
+        (dict(D=96), native.PA_ERR_UNSUPPORTED),
         (dict(dml=5), native.PA_ERR_INVALID),  # 5 rows x group 2 > 8
         (dict(dml=-2), native.PA_ERR_INVALID),
         (dict(split=-1), native.PA_ERR_INVALID),
