@@ -18,6 +18,9 @@ on the CPU" (nanoserve), "Week 2 Day 5: Fused Decode Attention" (tiny-llm)):
   mask, running max / denominator / weighted-V fold).
 - ``append.kv_append_ref`` -- the write half: new tokens' K/V copied into
   their page slots through the same translation.
+- ``masked.paged_attention_masked_ref`` / ``brute.paged_attention_masked_brute``
+  -- an explicit additive mask beside the causal flag ("Week 2 Day 5",
+  Tasks 1 and 2), vectorised and as scalar loops.
 - ``varlen.paged_attention_varlen_ref`` -- a mixed batch (each sequence its
   own query length, queries packed token-major): the definition applied to
   every sequence on its own.
@@ -35,7 +38,8 @@ from .reference import (
     validate,
     visible_mask,
 )
-from .brute import paged_attention_brute
+from .brute import paged_attention_brute, paged_attention_masked_brute
+from .masked import paged_attention_masked_ref
 from .online import paged_attention_online, tile_plan
 from .append import kv_append_ref
 from .varlen import paged_attention_varlen_ref, validate_varlen
@@ -49,6 +53,8 @@ __all__ = [
     "kv_head_of",
     "paged_attention_ref",
     "paged_attention_brute",
+    "paged_attention_masked_brute",
+    "paged_attention_masked_ref",
     "paged_attention_online",
     "tile_plan",
     "validate",

@@ -58,3 +58,51 @@ def paged_attention_brute(query, key_pages, value_pages, block_table, context_le
                     num = math.fsum(wi * vp[phys, g, slot, d] for wi, (_, phys, slot) in zip(w, keys))
                     out[b, h, l, d] = num / den
     return out
+
+
+def paged_attention_masked_brute(query, key_pages, value_pages, block_table, context_lens, mask, page_size, scale,
+                                 causal=True):
+    """Scalar loops with an explicit additive mask ``mask[b][h][l][s]`` (natural-log units).
+
+    A key is used when it is inside the context, allowed by the causal rule,
+    has a mask entry (s < the mask's last axis) and that entry is not -inf;
+    its score is scale * q.k plus the entry. A row with no usable key is NaN.
+    """
+    q = _widen(query).tolist()
+    kp = _widen(key_pages)
+    vp = _widen(value_pages)
+    B, Hq, L, D = np.asarray(query).shape
+    mk = np.broadcast_to(np.asarray(mask, dtype=np.float64), (B, Hq, L, np.asarray(mask).shape[3]))
+    S = mk.shape[3]
+    table = np.asarray(block_table).tolist()
+    ctxs = [int(c) for c in np.asarray(context_lens).tolist()]
+    Hkv = kp.shape[1]
+    group = Hq // Hkv
+    sc = float(np.float32(scale))
+    out = np.zeros((B, Hq, L, D), dtype=np.float64)
+    for b in range(B):
+        ctx = ctxs[b]
+        for h in range(Hq):
+            g = h // group
+            for l in range(L):
+                last = (l + ctx - L) if causal else (ctx - 1)
+                keys = []
+                for s in range(min(ctx, S)):
+                    add = float(mk[b, h, l, s])
+                    if s > last or add == -math.inf:
+                        continue
+                    phys = table[b][s // page_size]
+                    slot = s % page_size
+                    k = kp[phys, g, slot].tolist()
+                    dot = math.fsum(q[b][h][l][d] * k[d] for d in range(D))
+                    keys.append((sc * dot + add, phys, slot))
+                if not keys:
+                    out[b, h, l, :] = math.nan
+                    continue
+                mx = max(x for x, _, _ in keys)
+                w = [math.exp(x - mx) for x, _, _ in keys]
+                den = math.fsum(w)
+                for d in range(D):
+                    num = math.fsum(wi * vp[phys, g, slot, d] for wi, (_, phys, slot) in zip(w, keys))
+                    out[b, h, l, d] = num / den
+    return out
