@@ -218,6 +218,31 @@ class VarlenCase:
     time = Case.time
 
 
+class MaskedCase(Case):
+    """A problem through paged_attention_masked with a seeded additive mask of shape ``mshape``."""
+
+    def __init__(self, p, copies: int, mshape):
+        import numpy as np
+        import torch
+
+        super().__init__(p, copies)
+        rng = np.random.Generator(np.random.PCG64(2000 + p.seed))
+        m = rng.normal(0.0, 1.0, size=mshape).astype(np.float32)
+        m[rng.random(mshape) < 0.1] = -np.inf
+        m[..., 0] = 0.0
+        self.mask = torch.from_numpy(m).to("cuda:0")
+        # mask entries read: one per (row, head, visible key) for the axes the mask does not broadcast
+        B, Hq, L = p.batch, p.num_q_heads, p.query_len
+        per_key = (mshape[1] if mshape[1] > 1 else 1) * (mshape[2] if mshape[2] > 1 else 1)
+        self.mask_bytes = 4 * per_key * int(p.context_lens.astype(np.int64).sum()) if mshape[0] > 1 else None
+
+    def step(self):
+        k, v = self.pools[self.i % len(self.pools)]
+        self.i += 1
+        self._native.paged_attention_masked(self.q, k, v, self.bt, self.ctx, self.mask, self.p.page_size,
+                                            self.p.scale, self.p.causal, out=self.out, workspace=self.ws)
+
+
 def mixed_roofline_us(p) -> dict:
     """Lower bound of one mixed-batch call on this chip: the decode part's K/V bytes at HBM peak plus the
     prefill part's flops at the bf16 matrix peak (the two launches run one after the other)."""
@@ -410,6 +435,33 @@ def main():
             }
             del ca
             torch.cuda.empty_cache()
+        pdm = wl.make_config("decode_batch")
+        cdm = MaskedCase(pdm, POOL_COPIES, (64, 32, 1, 4096))
+        msd, _ = cdm.time(max(20, args.steps // 4), max(5, args.warmup // 4))
+        byt = pdm.kv_bytes() + cdm.mask_bytes
+        gd = byt / (msd * 1e-3) / 1e9
+        extra["masked_decode"] = {
+            "workload": "decode_batch with an explicit fp32 mask [64, 32, 1, 4096] (N(0,1) log-weights, 10% -inf)",
+            "ms_per_step": round(msd, 5), "value": round(gd / 1e3, 4), "unit": "TB/s",
+            "roofline": {"bound": "hbm", "achieved": round(gd, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gd / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_decode_work (masked)",
+                         "algorithmic_bytes_per_launch": byt, "mask_bytes": cdm.mask_bytes},
+        }
+        del cdm
+        torch.cuda.empty_cache()
+        ppm = wl.make_config("long_prefill")
+        cpm = MaskedCase(ppm, POOL_COPIES, (4, 1, 2048, 2048))
+        msp, _ = cpm.time(max(20, args.steps // 4), max(5, args.warmup // 4))
+        tfm = ppm.flops() / (msp * 1e-3) / 1e12
+        extra["masked_prefill"] = {
+            "workload": "long_prefill with an explicit fp32 mask [4, 1, 2048, 2048] shared by the heads",
+            "ms_per_step": round(msp, 5), "value": round(tfm, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tfm, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tfm / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "pa_prefill_mfma (masked)", "algorithmic_flops_per_launch": ppm.flops()},
+        }
+        del cpm
+        torch.cuda.empty_cache()
         pm = wl.make_varlen_config("mixed_batch")
         cm = VarlenCase(pm, 8)
         msm, _ = cm.time(max(20, args.steps // 2), max(5, args.warmup // 2))

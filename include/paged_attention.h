@@ -130,6 +130,43 @@ int paged_attention_ex(const void* query, const void* key_pages, const void* val
                        int32_t schedule, int32_t decode_work_items, void* stream);
 
 /*
+ * paged_attention_masked -- paged_attention_ex with an explicit additive
+ * mask beside the causal flag ("Week 2 Day 5: Fused Decode Attention",
+ * Task 1: the primitive accepts explicit masks normalised to
+ * [B * H_q, L, S]; Task 2, step 3: the scale, the optional mask and the
+ * causal check are applied to each score):
+ *
+ *   score[b,h,l,s] = scale * q[b,h,l,:] . K_b[s,:] + mask[b,h,l,s]
+ *
+ * for the keys s that the context and (with causal) the causal rule leave
+ * visible. The mask is in the units of the score (natural-log weights): -inf
+ * removes a key, a finite value multiplies its weight by exp(value).
+ *   mask          fp32, device. Entry (b, h, l, s) sits at element
+ *                 b*mask_stride_b + h*mask_stride_h + l*mask_stride_l + s;
+ *                 a stride of 0 broadcasts that axis (e.g. one mask row for
+ *                 every query head). The buffer must hold
+ *                 (B-1)*stride_b + (H_q-1)*stride_h + (L-1)*stride_l +
+ *                 mask_len floats. Entries must not be NaN.
+ *   mask_len      entries per mask row (the S axis), >= 1. A key at or past
+ *                 mask_len has no entry and is absent, so a short mask never
+ *                 leads to a read outside it.
+ * A row whose every key is absent (or -inf) has no softmax; its output is
+ * NaN, as 0 / 0 in the definition. Everything else -- arguments, layouts,
+ * schedules, workspace, errors -- as paged_attention_ex; additionally
+ * PA_ERR_INVALID for a NULL mask, a negative stride or mask_len < 1, or a
+ * mask that overlaps `out`. The masked kernel instances hold the mask
+ * entries in registers and run at lower occupancy than the unmasked ones.
+ */
+int paged_attention_masked(const void* query, const void* key_pages, const void* value_pages,
+                           const int32_t* block_table, const int32_t* context_lens, const float* mask,
+                           int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_l,
+                           int32_t mask_len, void* out, int32_t batch, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t query_len, int32_t head_dim, int32_t num_pages,
+                           int32_t page_size, int32_t max_pages, float scale, int32_t causal,
+                           void* workspace, size_t workspace_bytes, int32_t schedule,
+                           int32_t decode_work_items, void* stream);
+
+/*
  * Workspace bytes paged_attention (or paged_attention_ex with the same
  * schedule and decode_work_items) needs for these sizes; 0 when none is
  * needed.

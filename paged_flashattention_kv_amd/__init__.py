@@ -10,7 +10,7 @@ each sequence its own query length) in one call. PyTorch only provides
 device memory and streams.
 
 - ``native``    -- the ctypes binding (``paged_attention``,
-  ``paged_attention_varlen``, ``kv_append``, ``workspace_bytes``,
+  ``paged_attention_masked``, ``paged_attention_varlen``, ``kv_append``, ``workspace_bytes``,
   ``varlen_workspace_bytes``, ``schedule_for``, ``check_metadata``,
   ``check_varlen_metadata``)
 - ``workloads`` -- seeded synthetic inputs of the measured configurations
@@ -26,6 +26,7 @@ from .native import (  # noqa: F401
     check_varlen_metadata,
     kv_append,
     paged_attention,
+    paged_attention_masked,
     paged_attention_varlen,
     schedule_for,
     varlen_workspace_bytes,

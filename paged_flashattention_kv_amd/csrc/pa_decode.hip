@@ -103,6 +103,12 @@ struct DecodeArgs {
   int work_items;
   float c;  // scale * log2(e)
   int causal;
+  // Explicit additive mask (natural-log units) of row (b, h, l), key s at
+  // mask[b*msb + h*msh + l*msl + s] for s < mask_len; keys at or past
+  // mask_len are absent. Used by the MASKED instances only.
+  const float* mask;
+  int64_t msb, msh, msl;
+  int mask_len;
 };
 
 __device__ __forceinline__ int div_ps(int s, int ps, int ps_log2) { return ps_log2 >= 0 ? (s >> ps_log2) : s / ps; }
@@ -169,9 +175,25 @@ struct RowState {
   float acc[ROWS][16];
 };
 
+// The mask entries of one step for this lane's keys (t0 + kg + KPI*i) and
+// every row, loaded with the step's K/V. The index is clamped into the mask
+// row; entries of keys at or past mask_len are discarded in compute_stage.
 template <int ROWS, int D>
-__device__ __forceinline__ void compute_stage(const Stage& st, int t0, int s1, const uint32_t (&q)[ROWS][8],
-                                              const int (&last)[ROWS], int min_last, float c, int kg,
+__device__ __forceinline__ void load_mask(const float* const (&mrow)[ROWS], int mask_len, int t0, int kg,
+                                          float (&mv)[ROWS][kTK]) {
+  constexpr int KPI = Geo<D>::KPI;
+#pragma unroll
+  for (int i = 0; i < kTK; ++i) {
+    const int key = min(t0 + kg + KPI * i, mask_len - 1);
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) mv[r][i] = mrow[r][key];
+  }
+}
+
+template <int ROWS, int D, bool MASKED>
+__device__ __forceinline__ void compute_stage(const Stage& st, const float (&mv)[MASKED ? ROWS : 1][kTK], int t0,
+                                              int s1, int mask_len, const uint32_t (&q)[ROWS][8],
+                                              const int (&last)[ROWS], int min_last, float c_in, int kg,
                                               RowState<ROWS>& rs) {
   constexpr int LPK = Geo<D>::LPK, KPI = Geo<D>::KPI, kStep = Geo<D>::kStep;
   // scores (raw q.k): lane-partial bf16 dot products, summed over the key's LPK lanes
@@ -191,6 +213,20 @@ __device__ __forceinline__ void compute_stage(const Stage& st, int t0, int s1, c
       d = dot2_bf16(q[r][7], st.k[i][1].w, d);
       s[r][i] = sum_lanes<LPK>(d);
     }
+  }
+  // With a mask the score becomes scale * q.k + mask in log2 units here, and
+  // the softmax below takes it as is (c = 1); without one, the raw q.k and
+  // c = scale * log2(e) folded into the exponent argument.
+  float c = c_in;
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int i = 0; i < kTK; ++i) {
+      const int key = t0 + kg + KPI * i;
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r)
+        s[r][i] = key < mask_len ? fmaf(s[r][i], c_in, mv[r][i] * kLog2e) : -INFINITY;
+    }
+    c = 1.f;
   }
   // visibility: past the split end, or hidden by the causal rule (separate from the load)
   if (t0 + kStep > s1 || t0 + kStep - 1 > min_last) {
@@ -287,7 +323,7 @@ __device__ __forceinline__ int64_t gran_begin(int64_t w, int64_t total, int64_t 
 // rows of that kv head (sequence b has L rows from token `start`). Merges
 // the 4 waves' states and either stores the output (the piece is the whole
 // segment) or leaves the partial state in the workspace slot.
-template <int ROWS, bool ALIGNED, int D>
+template <int ROWS, bool ALIGNED, int D, bool MASKED>
 __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_bt, float (*lds_m)[ROWS],
                                              float (*lds_l)[ROWS], float (*lds_acc)[ROWS][D], int b, int kvh,
                                              int ctx, int L, int start, int k0, int k1, bool direct, int slot) {
@@ -302,11 +338,14 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
   const int rows = a.group * L;
   uint32_t q[ROWS][8];
   int last[ROWS];
+  const float* mrow[ROWS];  // mask row of each query row (MASKED only)
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
+    mrow[r] = a.mask;
     if (r < rows) {
       const int h = kvh * a.group + r / L;
       const int l = r % L;
+      if (MASKED) mrow[r] = a.mask + (size_t)b * a.msb + (size_t)h * a.msh + (size_t)l * a.msl;
       const uint16_t* qp = a.query + row_idx(a, b, start, L, h, l) * D;
       const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(qp + dc * 8);
       const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(qp + D / 2 + dc * 8);
@@ -366,14 +405,20 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
     int t = ka + wave * kStep;
     if (t < kb) {
       Stage st[kStages];
+      float mv[kStages][MASKED ? ROWS : 1][kTK];  // mask entries riding with each stage
 #pragma unroll
-      for (int i = 0; i < kStages - 1; ++i) load_stage<ALIGNED, D>(g, t + i * kStride, st[i]);
+      for (int i = 0; i < kStages - 1; ++i) {
+        load_stage<ALIGNED, D>(g, t + i * kStride, st[i]);
+        if constexpr (MASKED) load_mask<ROWS, D>(mrow, a.mask_len, t + i * kStride, kg, mv[i]);
+      }
       bool done = false;
       while (!done) {
 #pragma unroll
         for (int j = 0; j < kStages; ++j) {
           load_stage<ALIGNED, D>(g, t + (kStages - 1) * kStride, st[(j + kStages - 1) % kStages]);
-          compute_stage<ROWS, D>(st[j], t, kb, q, last, min_last, a.c, kg, rs);
+          if constexpr (MASKED)
+            load_mask<ROWS, D>(mrow, a.mask_len, t + (kStages - 1) * kStride, kg, mv[(j + kStages - 1) % kStages]);
+          compute_stage<ROWS, D, MASKED>(st[j], mv[j], t, kb, a.mask_len, q, last, min_last, a.c, kg, rs);
           t += kStride;
           if (t >= kb) {
             done = true;
@@ -515,7 +560,7 @@ __device__ void merge_segment(const DecodeArgs& a, int b, int kvh, int L, int st
   }
 }
 
-template <int ROWS, bool ALIGNED, int D>
+template <int ROWS, bool ALIGNED, int D, bool MASKED>
 __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
   extern __shared__ int32_t lds_bt[];
   __shared__ float lds_m[kWaves][ROWS];
@@ -580,7 +625,7 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
     const int k0 = (int)((G - S) * kGran);
     const int k1 = (int)min((gend - S) * kGran, (int64_t)ctx);
     const bool direct = G == S && gend == E;
-    decode_piece<ROWS, ALIGNED, D>(a, lds_bt, lds_m, lds_l, lds_acc, b, kvh, ctx, L, start, k0, k1, direct,
+    decode_piece<ROWS, ALIGNED, D, MASKED>(a, lds_bt, lds_m, lds_l, lds_acc, b, kvh, ctx, L, start, k0, k1, direct,
                                    nth == 0 ? 0 : 1);
     if (!direct) {
       // publish this piece, then the last of the segment's work items merges it
@@ -600,16 +645,16 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
   }
 }
 
-template <int ROWS, bool ALIGNED, int D>
+template <int ROWS, bool ALIGNED, int D, bool MASKED>
 hipError_t launch_work(const DecodeArgs& a, size_t lds_bytes, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_decode_work<ROWS, ALIGNED, D>), dim3((unsigned)a.work_items), dim3(kThreads), lds_bytes,
+  hipLaunchKernelGGL((pa_decode_work<ROWS, ALIGNED, D, MASKED>), dim3((unsigned)a.work_items), dim3(kThreads), lds_bytes,
                      stream, a);
   return hipGetLastError();
 }
 
 // Work items the GPU keeps resident for one kernel instance (cached per
 // device; registers, not shared memory, bound it for every page size).
-template <int ROWS, bool ALIGNED, int D>
+template <int ROWS, bool ALIGNED, int D, bool MASKED>
 int resident_items(size_t lds_bytes) {
   static int cache[64] = {0};
   int dev = 0;
@@ -617,7 +662,7 @@ int resident_items(size_t lds_bytes) {
   if (cache[dev] > 0) return cache[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)pa_decode_work<ROWS, ALIGNED, D>, kThreads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)pa_decode_work<ROWS, ALIGNED, D, MASKED>, kThreads,
                                                    lds_bytes) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   const int n = cus * per_cu;
@@ -625,24 +670,29 @@ int resident_items(size_t lds_bytes) {
   return n;
 }
 
-template <int ROWS, int D>
+template <int ROWS, int D, bool MASKED>
 hipError_t launch_rows(DecodeArgs& a, bool aligned, int requested, int cap, size_t lds, hipStream_t st) {
   if (aligned) {
-    a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, true, D>(lds));
-    return launch_work<ROWS, true, D>(a, lds, st);
+    a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, true, D, MASKED>(lds));
+    return launch_work<ROWS, true, D, MASKED>(a, lds, st);
   }
-  a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, false, D>(lds));
-  return launch_work<ROWS, false, D>(a, lds, st);
+  a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, false, D, MASKED>(lds));
+  return launch_work<ROWS, false, D, MASKED>(a, lds, st);
+}
+
+template <int D, bool MASKED>
+hipError_t launch_mask(DecodeArgs& a, const Plan& p, size_t lds, hipStream_t stream) {
+  switch (p.rows_pad) {
+    case 1: return launch_rows<1, D, MASKED>(a, p.aligned, p.work_items, p.work_cap, lds, stream);
+    case 2: return launch_rows<2, D, MASKED>(a, p.aligned, p.work_items, p.work_cap, lds, stream);
+    case 4: return launch_rows<4, D, MASKED>(a, p.aligned, p.work_items, p.work_cap, lds, stream);
+    default: return launch_rows<8, D, MASKED>(a, p.aligned, p.work_items, p.work_cap, lds, stream);
+  }
 }
 
 template <int D>
 hipError_t launch_dim(DecodeArgs& a, const Plan& p, size_t lds, hipStream_t stream) {
-  switch (p.rows_pad) {
-    case 1: return launch_rows<1, D>(a, p.aligned, p.work_items, p.work_cap, lds, stream);
-    case 2: return launch_rows<2, D>(a, p.aligned, p.work_items, p.work_cap, lds, stream);
-    case 4: return launch_rows<4, D>(a, p.aligned, p.work_items, p.work_cap, lds, stream);
-    default: return launch_rows<8, D>(a, p.aligned, p.work_items, p.work_cap, lds, stream);
-  }
+  return a.mask ? launch_mask<D, true>(a, p, lds, stream) : launch_mask<D, false>(a, p, lds, stream);
 }
 
 }  // namespace
@@ -673,6 +723,11 @@ hipError_t launch_decode(const KernelArgs& k, const Plan& p, hipStream_t stream)
   a.epoch = k.epoch;
   a.qstart = k.query_start;
   a.total_query = k.total_query;
+  a.mask = k.mask;
+  a.msb = k.mask_stride_b;
+  a.msh = k.mask_stride_h;
+  a.msl = k.mask_stride_l;
+  a.mask_len = k.mask_len;
   if (k.query_start) a.query_len = k.dec_max_len;  // the longest query this launch serves
   const size_t lds = (size_t)p.bt_entries * sizeof(int32_t);
   switch (k.head_dim) {

@@ -31,6 +31,13 @@ struct KernelArgs {
   const int32_t* query_start = nullptr;
   int total_query = 0;
   int dec_max_len = 0;
+  // Explicit additive mask (natural-log units, uniform layout only): row
+  // (b, h, l), key s at mask[b*mask_stride_b + h*mask_stride_h +
+  // l*mask_stride_l + s] for s < mask_len; keys at or past mask_len are
+  // absent. nullptr: no mask.
+  const float* mask = nullptr;
+  int64_t mask_stride_b = 0, mask_stride_h = 0, mask_stride_l = 0;
+  int mask_len = 0;
 };
 
 // Short-query split-context schedule (pa_decode.hip).

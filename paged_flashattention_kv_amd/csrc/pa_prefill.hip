@@ -97,6 +97,13 @@ struct PrefillArgs {
   int page_size, ps_log2, max_pages;
   float c;  // scale * log2(e)
   int causal;
+  // Explicit additive mask (natural-log units, uniform layout): row (b, h, l),
+  // key s at mask[b*msb + h*msh + l*msl + s] for s < mask_len; keys at or past
+  // mask_len are absent. Used by the MASKED instances only.
+  const float* mask;
+  int64_t msb, msh, msl;
+  int mask_len;
+  int mask_vec;  // every mask row starts 16-byte aligned: four keys per load
 };
 
 __device__ __forceinline__ int div_ps(int s, int ps, int ps_log2) { return ps_log2 >= 0 ? (s >> ps_log2) : s / ps; }
@@ -179,8 +186,8 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages
 
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <bool ALIGNED, int D>
-__global__ void __launch_bounds__(kThreads, Tile<D>::kBlocksPerCU) pa_prefill_mfma(PrefillArgs a) {
+template <bool ALIGNED, int D, bool MASKED>
+__global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) pa_prefill_mfma(PrefillArgs a) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(1024))) char lds_k0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char lds_k1[T::kBytes];
@@ -278,6 +285,10 @@ __global__ void __launch_bounds__(kThreads, Tile<D>::kBlocksPerCU) pa_prefill_mf
   const uint32_t ones_bf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
   const int row_abs = r0 + col;
+  // this lane's mask row (MASKED only; rows past L read row L - 1, never stored)
+  const float* mrow = a.mask;
+  if (MASKED)
+    mrow = a.mask + (size_t)b * a.msb + (size_t)head * a.msh + (size_t)(row_abs < L ? row_abs : L - 1) * a.msl;
   // One tile: wait for its loads, barrier, start the next tile's loads into
   // the other buffer, compute. The buffers are distinct LDS objects chosen
   // statically (the loop is unrolled by two), so no wait is needed between
@@ -286,10 +297,35 @@ __global__ void __launch_bounds__(kThreads, Tile<D>::kBlocksPerCU) pa_prefill_mf
     const int t0 = t * kBN;
     wait_all_loads();  // this wave's part of tile t (and the next lookup) has landed
     __syncthreads();   // every wave's part is in LDS; every wave is done with tile t - 1
+    const bool active = wave_has_rows && t0 < wave_kv_end;
+    // mask entries of this lane's row for the tile's keys; issued before the
+    // next tile's loads so that waiting for them does not wait for those
+    float mvals[MASKED ? 2 : 1][16];
+    if constexpr (MASKED) {
+      if (active) {
+        // elements 4j .. 4j+3 of a block are four consecutive keys (a multiple of 4 first)
+  #pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int k0 = t0 + 32 * kb + 8 * j + 4 * half;
+            if (a.mask_vec && k0 + 3 < a.mask_len) {
+              const f32x4_t v = *reinterpret_cast<const f32x4_t*>(mrow + k0);
+              mvals[kb][4 * j] = v.x;
+              mvals[kb][4 * j + 1] = v.y;
+              mvals[kb][4 * j + 2] = v.z;
+              mvals[kb][4 * j + 3] = v.w;
+            } else {
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) mvals[kb][4 * j + e] = mrow[min(k0 + e, a.mask_len - 1)];
+            }
+          }
+      }
+    }
     if (t + 1 < n_tiles) issue_tile<ALIGNED, D>(a, tp, ctx, t0 + kBN, wave, lane, knext, vnext);
     // lookup for tile t + 2 (clamped so that it is unconditional)
     lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, min(t + 2, n_tiles - 1) * kBN, wave, lane, tp);
-    if (!wave_has_rows || t0 >= wave_kv_end) return;
+    if (!active) return;
 
       // ---- S^T = K Q^T : two 32-key blocks ----
       f32x16_t acc_s[2];
@@ -308,8 +344,20 @@ __global__ void __launch_bounds__(kThreads, Tile<D>::kBlocksPerCU) pa_prefill_mf
 
       // ---- mask, online softmax (row = this lane's query row) ----
       // element i of block kb is key 32kb + 8(i/4) + 4half + i%4 of the tile.
-      // The maximum is taken on raw scores (c > 0); the scale is folded into
-      // the exponent argument.
+      // Without an explicit mask the maximum is taken on raw scores (c > 0)
+      // and the scale is folded into the exponent argument; with one, each
+      // score becomes scale * q.k + mask in log2 units first (cs = 1).
+      float cs = a.c;
+      if constexpr (MASKED) {
+  #pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = t0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+            acc_s[kb][i] = key < a.mask_len ? fmaf(acc_s[kb][i], a.c, mvals[kb][i] * kLog2e) : -INFINITY;
+          }
+        cs = 1.f;
+      }
       const bool need_mask = (t0 + kBN > ctx) || (a.causal && t0 + kBN - 1 > r0 + offset);
       if (need_mask) {
   #pragma unroll
@@ -332,7 +380,7 @@ __global__ void __launch_bounds__(kThreads, Tile<D>::kBlocksPerCU) pa_prefill_mf
         const float m4 = fmaxf(fmaxf(acc_s[kb][12], acc_s[kb][13]), acc_s[kb][14]);
         mx[kb] = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), acc_s[kb][15]));
       }
-      const float tmax = max_xor32(fmaxf(mx[0], mx[1])) * a.c;  // log2 units
+      const float tmax = max_xor32(fmaxf(mx[0], mx[1])) * cs;  // log2 units
       // The exponent reference moves only when the tile maximum exceeds it by
       // more than kTau; otherwise the weights stay <= 2^kTau and the output
       // needs no rescale. The branch is taken when any row of the wave moves.
@@ -353,8 +401,8 @@ __global__ void __launch_bounds__(kThreads, Tile<D>::kBlocksPerCU) pa_prefill_mf
       for (int kb = 0; kb < 2; ++kb) {
   #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const float p0 = fast_exp2(fmaf(acc_s[kb][i], a.c, neg_ref));
-          const float p1 = fast_exp2(fmaf(acc_s[kb][i + 1], a.c, neg_ref));
+          const float p0 = fast_exp2(fmaf(acc_s[kb][i], cs, neg_ref));
+          const float p1 = fast_exp2(fmaf(acc_s[kb][i + 1], cs, neg_ref));
           pk[kb][i >> 1] = pack_bf16x2(p0, p1);
           psum = dot2_bf16(pk[kb][i >> 1], ones_bf16x2, psum);  // the weights the MFMA uses
         }
@@ -408,13 +456,18 @@ __global__ void __launch_bounds__(kThreads, Tile<D>::kBlocksPerCU) pa_prefill_mf
   }
 }
 
+template <int D, bool MASKED>
+hipError_t launch_mask(const PrefillArgs& a, const Plan& p, hipStream_t stream) {
+  if (p.aligned)
+    hipLaunchKernelGGL((pa_prefill_mfma<true, D, MASKED>), dim3((unsigned)p.num_work), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((pa_prefill_mfma<false, D, MASKED>), dim3((unsigned)p.num_work), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_dim(const PrefillArgs& a, const Plan& p, hipStream_t stream) {
-  if (p.aligned)
-    hipLaunchKernelGGL((pa_prefill_mfma<true, D>), dim3((unsigned)p.num_work), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((pa_prefill_mfma<false, D>), dim3((unsigned)p.num_work), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return a.mask ? launch_mask<D, true>(a, p, stream) : launch_mask<D, false>(a, p, stream);
 }
 
 }  // namespace
@@ -441,6 +494,13 @@ hipError_t launch_prefill(const KernelArgs& k, const Plan& p, hipStream_t stream
   a.qstart = k.query_start;
   a.total_query = k.total_query;
   a.skip_len = k.query_start ? k.dec_max_len : 0;
+  a.mask = k.mask;
+  a.msb = k.mask_stride_b;
+  a.msh = k.mask_stride_h;
+  a.msl = k.mask_stride_l;
+  a.mask_len = k.mask_len;
+  a.mask_vec = k.mask && (reinterpret_cast<uintptr_t>(k.mask) % 16 == 0) && k.mask_stride_b % 4 == 0 &&
+               k.mask_stride_h % 4 == 0 && k.mask_stride_l % 4 == 0;
   switch (k.head_dim) {
     case 64: return launch_dim<64>(a, p, stream);
     case 256: return launch_dim<256>(a, p, stream);

@@ -52,16 +52,19 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
-}  // namespace
+// An explicit mask of the uniform entry points.
+struct MaskSpec {
+  const float* ptr;
+  int64_t sb, sh, sl;
+  int32_t len;
+};
 
-extern "C" {
-
-int paged_attention_ex(const void* query, const void* key_pages, const void* value_pages,
-                       const int32_t* block_table, const int32_t* context_lens, void* out,
-                       int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t query_len,
-                       int32_t head_dim, int32_t num_pages, int32_t page_size, int32_t max_pages,
-                       float scale, int32_t causal, void* workspace, size_t workspace_bytes,
-                       int32_t schedule, int32_t decode_work_items, void* stream) {
+// The uniform-layout operator, with or without an explicit mask.
+int run_uniform(const void* query, const void* key_pages, const void* value_pages, const int32_t* block_table,
+                const int32_t* context_lens, const MaskSpec* mask, void* out, int32_t batch, int32_t num_q_heads,
+                int32_t num_kv_heads, int32_t query_len, int32_t head_dim, int32_t num_pages, int32_t page_size,
+                int32_t max_pages, float scale, int32_t causal, void* workspace, size_t workspace_bytes,
+                int32_t schedule, int32_t decode_work_items, void* stream) {
   if (!query || !key_pages || !value_pages || !block_table || !context_lens || !out)
     return set_error(PA_ERR_INVALID, "a tensor pointer is NULL");
   if (causal != 0 && causal != 1) return set_error(PA_ERR_INVALID, "causal must be 0 or 1");
@@ -83,6 +86,12 @@ int paged_attention_ex(const void* query, const void* key_pages, const void* val
       overlaps(out, q_bytes, context_lens, size_t(batch) * 4) ||
       (plan.workspace_bytes > 0 && overlaps(out, q_bytes, workspace, plan.workspace_bytes)))
     return set_error(PA_ERR_INVALID, "out overlaps an input or the workspace");
+  if (mask) {
+    // the mask buffer spans (B-1)*sb + (H_q-1)*sh + (L-1)*sl + len floats
+    const size_t span = size_t((batch - 1) * mask->sb + (num_q_heads - 1) * mask->sh +
+                               (query_len - 1) * mask->sl + mask->len) * sizeof(float);
+    if (overlaps(out, q_bytes, mask->ptr, span)) return set_error(PA_ERR_INVALID, "out overlaps the mask");
+  }
 
   pa::KernelArgs k;
   k.query = query;
@@ -103,12 +112,55 @@ int paged_attention_ex(const void* query, const void* key_pages, const void* val
   k.scale = scale;
   k.causal = causal;
   k.epoch = next_epoch();
+  if (mask) {
+    k.mask = mask->ptr;
+    k.mask_stride_b = mask->sb;
+    k.mask_stride_h = mask->sh;
+    k.mask_stride_l = mask->sl;
+    k.mask_len = mask->len;
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = plan.schedule == pa::kScheduleDecode ? pa::launch_decode(k, plan, st)
                                                             : pa::launch_prefill(k, plan, st);
   if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, std::string("launch failed: ") + hipGetErrorString(e));
   g_last_error.clear();
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_ex(const void* query, const void* key_pages, const void* value_pages,
+                       const int32_t* block_table, const int32_t* context_lens, void* out,
+                       int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t query_len,
+                       int32_t head_dim, int32_t num_pages, int32_t page_size, int32_t max_pages,
+                       float scale, int32_t causal, void* workspace, size_t workspace_bytes,
+                       int32_t schedule, int32_t decode_work_items, void* stream) {
+  return run_uniform(query, key_pages, value_pages, block_table, context_lens, nullptr, out, batch, num_q_heads,
+                     num_kv_heads, query_len, head_dim, num_pages, page_size, max_pages, scale, causal, workspace,
+                     workspace_bytes, schedule, decode_work_items, stream);
+}
+
+int paged_attention_masked(const void* query, const void* key_pages, const void* value_pages,
+                           const int32_t* block_table, const int32_t* context_lens, const float* mask,
+                           int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_l,
+                           int32_t mask_len, void* out, int32_t batch, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t query_len, int32_t head_dim, int32_t num_pages,
+                           int32_t page_size, int32_t max_pages, float scale, int32_t causal,
+                           void* workspace, size_t workspace_bytes, int32_t schedule,
+                           int32_t decode_work_items, void* stream) {
+  if (!mask) return set_error(PA_ERR_INVALID, "mask is NULL");
+  if (mask_stride_b < 0 || mask_stride_h < 0 || mask_stride_l < 0)
+    return set_error(PA_ERR_INVALID, "mask strides must be >= 0");
+  if (mask_len < 1) return set_error(PA_ERR_INVALID, "mask_len must be positive");
+  const int64_t lim = int64_t(1) << 40;  // keeps the extent arithmetic far from overflow
+  if (mask_stride_b > lim || mask_stride_h > lim || mask_stride_l > lim)
+    return set_error(PA_ERR_UNSUPPORTED, "mask strides too large");
+  const MaskSpec m{mask, mask_stride_b, mask_stride_h, mask_stride_l, mask_len};
+  return run_uniform(query, key_pages, value_pages, block_table, context_lens, &m, out, batch, num_q_heads,
+                     num_kv_heads, query_len, head_dim, num_pages, page_size, max_pages, scale, causal, workspace,
+                     workspace_bytes, schedule, decode_work_items, stream);
 }
 
 int paged_attention(const void* query, const void* key_pages, const void* value_pages,

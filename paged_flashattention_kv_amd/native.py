@@ -42,6 +42,7 @@ EXPORTED = (
     "paged_attention_varlen_ex",
     "paged_attention_varlen_workspace_bytes",
     "paged_attention_varlen_check_metadata",
+    "paged_attention_masked",
 )
 
 _lib = None
@@ -91,6 +92,10 @@ def load() -> ctypes.CDLL:
         lib.paged_attention_varlen_workspace_bytes.restype = sz
         lib.paged_attention_varlen_check_metadata.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
         lib.paged_attention_varlen_check_metadata.restype = ctypes.c_int
+        i64 = ctypes.c_int64
+        lib.paged_attention_masked.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32, i32,
+                                               i32, i32, i32, i32, f32, i32, vp, sz, i32, i32, vp]
+        lib.paged_attention_masked.restype = ctypes.c_int
         lib.paged_attention_last_error.argtypes = []
         lib.paged_attention_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -368,3 +373,81 @@ def check_varlen_metadata(block_table: torch.Tensor, context_lens: torch.Tensor,
         _stream_ptr(stream, dev),
     )
     _check(rc)
+
+
+def paged_attention_masked(
+    query: torch.Tensor,
+    key_pages: torch.Tensor,
+    value_pages: torch.Tensor,
+    block_table: torch.Tensor,
+    context_lens: torch.Tensor,
+    mask: torch.Tensor,
+    page_size: int,
+    scale: Optional[float] = None,
+    causal: bool = True,
+    *,
+    out: Optional[torch.Tensor] = None,
+    workspace: Optional[torch.Tensor] = None,
+    schedule: int = SCHEDULE_AUTO,
+    decode_work_items: int = 0,
+    stream: Optional[torch.cuda.Stream] = None,
+) -> torch.Tensor:
+    """Paged attention with an explicit additive mask beside the causal flag.
+
+    ``mask`` is a float32 GPU tensor of 4 axes [B or 1, H_q or 1, L or 1, S]
+    (an axis of size 1 -- or an expanded view -- broadcasts), natural-log
+    units, last axis contiguous: score = scale * q.k + mask; -inf removes a
+    key, keys at or past S are absent ("Week 2 Day 5: Fused Decode
+    Attention", Tasks 1-2). Other arguments as :func:`paged_attention`.
+    """
+    dev = query.device
+    if dev.type != "cuda":
+        raise ValueError("query must be a GPU tensor")
+    _require(query, "query", torch.bfloat16, 4, dev)
+    _require(key_pages, "key_pages", torch.bfloat16, 4, dev)
+    _require(value_pages, "value_pages", torch.bfloat16, 4, dev)
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(context_lens, "context_lens", torch.int32, 1, dev)
+    if not isinstance(mask, torch.Tensor) or mask.dtype != torch.float32 or mask.dim() != 4 or mask.device != dev:
+        raise TypeError("mask must be a 4-axis float32 tensor on the query's device")
+    B, Hq, L, D = query.shape
+    for ax, (n, full) in enumerate(zip(mask.shape[:3], (B, Hq, L))):
+        if n not in (1, full):
+            raise ValueError(f"mask axis {ax} has size {n}, expected 1 or {full}")
+    if mask.shape[3] < 1 or (mask.shape[3] > 1 and mask.stride(3) != 1):
+        raise ValueError("the mask's last axis must be non-empty and contiguous")
+    strides = [0 if mask.shape[i] == 1 else mask.stride(i) for i in range(3)]
+    if min(strides) < 0:
+        raise ValueError("negative mask strides are not supported")
+    P, Hkv, ps, Dk = key_pages.shape
+    if tuple(value_pages.shape) != tuple(key_pages.shape):
+        raise ValueError("key_pages and value_pages must have the same shape")
+    if ps != page_size or Dk != D:
+        raise ValueError("page pool shape does not match page_size / head_dim")
+    if block_table.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_table and context_lens need one row per sequence")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty_like(query)
+    else:
+        _require(out, "out", torch.bfloat16, 4, dev)
+        if tuple(out.shape) != tuple(query.shape):
+            raise ValueError("out must have the query's shape")
+    need = workspace_bytes(B, Hq, Hkv, L, D, ps, max_pages, schedule, decode_work_items)
+    ws_ptr, ws_len = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the query's device")
+        ws_ptr, ws_len = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rc = load().paged_attention_masked(
+        query.data_ptr(), key_pages.data_ptr(), value_pages.data_ptr(), block_table.data_ptr(),
+        context_lens.data_ptr(), mask.data_ptr(), strides[0], strides[1], strides[2], int(mask.shape[3]),
+        out.data_ptr(), B, Hq, Hkv, L, D, P, ps, max_pages, float(scale), 1 if causal else 0, ws_ptr, ws_len,
+        int(schedule), int(decode_work_items), _stream_ptr(stream, dev),
+    )
+    _check(rc)
+    return out

@@ -31,7 +31,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     assert sorted(native.EXPORTED) == names
     raw = ctypes.CDLL(native.LIB_PATH)
     for n in names:
@@ -143,6 +143,36 @@ def _varlen(lib, **kw):
 )
 def test_varlen_invalid_arguments_return_codes(lib, kw, code):
     assert _varlen(lib, **kw) == code
+    assert native.last_error() != ""
+
+
+def _masked(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, bt=FAKE + 0x300000, cl=FAKE + 0x400000,
+             m=FAKE + 0x600000, sb=0, sh=0, sl=0, mlen=64, out=FAKE + 0x500000, B=1, Hq=4, Hkv=2, L=1, D=128, P=8,
+             ps=16, mp=4, scale=0.088, causal=1, ws=None, wsb=0, sched=2, split=0)
+    a.update(kw)
+    return lib.paged_attention_masked(a["q"], a["k"], a["v"], a["bt"], a["cl"], a["m"], a["sb"], a["sh"], a["sl"],
+                                      a["mlen"], a["out"], a["B"], a["Hq"], a["Hkv"], a["L"], a["D"], a["P"], a["ps"],
+                                      a["mp"], a["scale"], a["causal"], a["ws"], a["wsb"], a["sched"], a["split"],
+                                      None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(m=None), native.PA_ERR_INVALID),
+        (dict(sb=-1), native.PA_ERR_INVALID),
+        (dict(sl=-64), native.PA_ERR_INVALID),
+        (dict(mlen=0), native.PA_ERR_INVALID),
+        (dict(sh=1 << 41), native.PA_ERR_UNSUPPORTED),
+        (dict(D=96), native.PA_ERR_UNSUPPORTED),
+        (dict(q=None), native.PA_ERR_INVALID),
+        (dict(out=FAKE + 0x600000 + 128), native.PA_ERR_INVALID),  # out inside the mask
+        (dict(sched=0), native.PA_ERR_WORKSPACE),  # decode schedule without workspace
+    ],
+)
+def test_masked_invalid_arguments_return_codes(lib, kw, code):
+    assert _masked(lib, **kw) == code
     assert native.last_error() != ""
 
 
