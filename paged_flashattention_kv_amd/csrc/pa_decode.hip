@@ -510,7 +510,9 @@ __device__ __forceinline__ bool arrive_last(uint64_t* ctr, uint32_t epoch, uint3
 }
 
 // The work items holding pieces of segment [S, E) (granules) and the number
-// of non-empty ones.
+// of non-empty ones. With at least as many granules as work items every work
+// item holds one or more granules; with fewer, every non-empty work item holds
+// exactly one, so the segment's E - S granules sit in E - S work items.
 struct SegmentItems {
   int64_t wf, wl;
   uint32_t count;
@@ -520,43 +522,78 @@ __device__ __forceinline__ SegmentItems segment_items(int64_t S, int64_t E, int6
   SegmentItems it;
   it.wf = ((S + 1) * P - 1) / total;  // work item holding granule S
   it.wl = (E * P - 1) / total;        // work item holding granule E - 1
-  it.count = 0;
-  for (int64_t w = it.wf; w <= it.wl; ++w) it.count += gran_begin(w, total, P) < gran_begin(w + 1, total, P);
+  it.count = (uint32_t)(total >= P ? it.wl - it.wf + 1 : E - S);
   return it;
 }
 
 // Combines the partial states of one shared segment ("Week 2 Day 5", Task 2:
 // common maximum, one rescale factor per partial, one denominator, the head
 // dimensions in parallel). Work item w's piece sits in slot 0 when the
-// segment is the first piece of w's range, else in slot 1. Partials with
-// maximum -inf (no visible key) contribute 0.
+// segment is the first piece of w's range, else in slot 1. The slot index of
+// every work item of the segment (-1 for an empty one) is listed in LDS, up
+// to kThreads at a time; each thread then folds kMergeBatch partials per
+// round, with all of their loads issued before the first is used. Partials
+// with maximum -inf (no visible key) contribute 0.
+constexpr int kMergeBatch = 8;
+
 template <int D>
-__device__ void merge_segment(const DecodeArgs& a, int b, int kvh, int L, int start, int64_t S,
+__device__ void merge_segment(const DecodeArgs& a, int32_t* lds_parts, int b, int kvh, int L, int start, int64_t S,
                               const SegmentItems& it, int64_t total) {
   const int64_t P = a.work_items;
-  for (int idx = threadIdx.x; idx < a.group * L * D; idx += kThreads) {
-    const int r = idx / D;
+  const int n_rd = a.group * L * D;
+  const int64_t n_w = it.wl - it.wf + 1;
+  const int tid = threadIdx.x;
+  for (int base = 0; base < n_rd; base += kThreads) {  // uniform trip count (barriers inside)
+    const int idx = base + tid;
+    const int r = idx < n_rd ? idx / D : 0;
     const int d = idx % D;
-    float M = -INFINITY;
-    for (int64_t w = it.wf; w <= it.wl; ++w) {
-      const int64_t gw = gran_begin(w, total, P);
-      if (gw == gran_begin(w + 1, total, P)) continue;  // empty work item
-      const size_t part = ((size_t)w * 2 + (gw >= S ? 0 : 1)) * a.rows + r;
-      M = fmaxf(M, load_coherent(a.ws_ml + part * 2));
+    float M = -INFINITY, den = 0.f, num = 0.f;
+    for (int64_t c0 = 0; c0 < n_w; c0 += kThreads) {
+      const int nc = (int)min((int64_t)kThreads, n_w - c0);
+      __syncthreads();  // the previous list is no longer read
+      if (tid < nc) {
+        const int64_t w = it.wf + c0 + tid;
+        const int64_t gw = gran_begin(w, total, P);
+        lds_parts[tid] = gw < gran_begin(w + 1, total, P) ? (int)(w * 2 + (gw >= S ? 0 : 1)) : -1;
+      }
+      __syncthreads();
+      for (int j0 = 0; j0 < nc; j0 += kMergeBatch) {
+        float mj[kMergeBatch], lj[kMergeBatch], aj[kMergeBatch];
+        bool ok[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+          const int pi = lds_parts[min(j0 + u, nc - 1)];
+          ok[u] = j0 + u < nc && pi >= 0;
+          const size_t part = (size_t)(pi > 0 ? pi : 0) * a.rows + r;  // slot 0 of item 0: a valid address
+          mj[u] = load_coherent(a.ws_ml + part * 2);
+          lj[u] = load_coherent(a.ws_ml + part * 2 + 1);
+          aj[u] = load_coherent(a.ws_acc + part * D + d);
+        }
+        float Mb = M;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+          mj[u] = ok[u] ? mj[u] : -INFINITY;
+          Mb = fmaxf(Mb, mj[u]);
+        }
+        if (Mb > -INFINITY) {
+          const float fo = M == -INFINITY ? 0.f : fast_exp2(M - Mb);
+          den *= fo;
+          num *= fo;
+#pragma unroll
+          for (int u = 0; u < kMergeBatch; ++u) {
+            const float f = mj[u] == -INFINITY ? 0.f : fast_exp2(mj[u] - Mb);
+            den = fmaf(f, ok[u] ? lj[u] : 0.f, den);
+            num = fmaf(f, ok[u] ? aj[u] : 0.f, num);
+          }
+          M = Mb;
+        }
+      }
     }
-    float den = 0.f, num = 0.f;
-    for (int64_t w = it.wf; w <= it.wl; ++w) {
-      const int64_t gw = gran_begin(w, total, P);
-      if (gw == gran_begin(w + 1, total, P)) continue;
-      const size_t part = ((size_t)w * 2 + (gw >= S ? 0 : 1)) * a.rows + r;
-      const float mj = load_coherent(a.ws_ml + part * 2);
-      const float f = mj == -INFINITY ? 0.f : fast_exp2(mj - M);
-      den = fmaf(f, load_coherent(a.ws_ml + part * 2 + 1), den);
-      num = fmaf(f, load_coherent(a.ws_acc + part * D + d), num);
+    if (idx < n_rd) {
+      const int h = kvh * a.group + r / L;
+      const int l = r % L;
+      a.out[row_idx(a, b, start, L, h, l) * D + d] = to_bf16(num / den);
     }
-    const int h = kvh * a.group + r / L;
-    const int l = r % L;
-    a.out[row_idx(a, b, start, L, h, l) * D + d] = to_bf16(num / den);
   }
 }
 
@@ -568,6 +605,7 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
   __shared__ float lds_acc[kWaves][ROWS][D];
   __shared__ int64_t lds_scan[kThreads];
   __shared__ int64_t lds_start[2];  // (sequence holding the first granule, its granule prefix)
+  __shared__ int32_t lds_parts[kThreads];  // partial slots of the segment being merged
   __shared__ bool lds_last;
 
   const int tid = threadIdx.x;
@@ -634,7 +672,7 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
       const SegmentItems it = segment_items(S, E, total, a.work_items);
       if (tid == 0) lds_last = arrive_last(a.ws_ctr + (size_t)b * a.num_kv_heads + kvh, a.epoch, it.count);
       __syncthreads();
-      if (lds_last) merge_segment<D>(a, b, kvh, L, start, S, it, total);
+      if (lds_last) merge_segment<D>(a, lds_parts, b, kvh, L, start, S, it, total);
     }
     G = gend;
     ++nth;

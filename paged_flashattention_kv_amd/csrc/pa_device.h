@@ -53,42 +53,18 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, false));
 }
 
-// Sum over the N consecutive lanes of an aligned group of N (N = 4, 8 or
-// 16); every lane of the group receives the total.
+// Sum over the N consecutive lanes of an aligned group of N (N = 4, 8, 16
+// or 32); every lane of the group receives the total.
 template <int N>
 __device__ __forceinline__ float sum_lanes(float x) {
-  static_assert(N == 4 || N == 8 || N == 16, "groups of 4, 8 or 16 lanes");
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "groups of 4, 8, 16 or 32 lanes");
   x += dpp<kDppQuadXor1>(x);
   x += dpp<kDppQuadXor2>(x);
   if (N >= 8) x += dpp<kDppRowHalfMirror>(x);
   if (N >= 16) x += dpp<kDppRowMirror>(x);
+  if (N >= 32) x += __shfl_xor(x, 16);
   return x;
 }
-
-// Reductions over the lanes that share (lane % S) (S = 4, 8 or 16): the orbit
-// of lane i under rotations by S inside its 16-lane DPP row, then xor 16 and
-// 32 across rows.
-template <int S>
-__device__ __forceinline__ float max_stride(float x) {
-  static_assert(S == 4 || S == 8 || S == 16, "strides of 4, 8 or 16 lanes");
-  if (S == 4) x = fmaxf(x, dpp<kDppRowRor4>(x));
-  if (S <= 8) x = fmaxf(x, dpp<kDppRowRor8>(x));
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-
-template <int S>
-__device__ __forceinline__ float sum_stride(float x) {
-  static_assert(S == 4 || S == 8 || S == 16, "strides of 4, 8 or 16 lanes");
-  if (S == 4) x += dpp<kDppRowRor4>(x);
-  if (S <= 8) x += dpp<kDppRowRor8>(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Max / sum of x over the lane pair (l, l ^ 32): v_permlane32_swap hands
 // every lane the values of lanes l % 32 and l % 32 + 32.
@@ -100,5 +76,28 @@ __device__ __forceinline__ float sum_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
+
+// Reductions over the lanes that share (lane % S) (S = 4, 8, 16 or 32): the
+// orbit of lane i under rotations by S inside its 16-lane DPP row, then xor
+// 16 and 32 across rows.
+template <int S>
+__device__ __forceinline__ float max_stride(float x) {
+  static_assert(S == 4 || S == 8 || S == 16 || S == 32, "strides of 4, 8, 16 or 32 lanes");
+  if (S == 4) x = fmaxf(x, dpp<kDppRowRor4>(x));
+  if (S <= 8) x = fmaxf(x, dpp<kDppRowRor8>(x));
+  if (S <= 16) x = fmaxf(x, __shfl_xor(x, 16));
+  return max_xor32(x);
+}
+
+template <int S>
+__device__ __forceinline__ float sum_stride(float x) {
+  static_assert(S == 4 || S == 8 || S == 16 || S == 32, "strides of 4, 8, 16 or 32 lanes");
+  if (S == 4) x += dpp<kDppRowRor4>(x);
+  if (S <= 8) x += dpp<kDppRowRor8>(x);
+  if (S <= 16) x += __shfl_xor(x, 16);
+  return sum_xor32(x);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace pa
