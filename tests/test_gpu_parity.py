@@ -262,6 +262,22 @@ def test_prefill_query_tiles_and_offsets(L):
     parity(run_gpu(p, schedule=PREFILL), ref(p), f"prefill L={L}")
 
 
+# Long queries: many 128-row query tiles with a ragged last one, both
+# loaders, chunked continuations and non-causal attention.
+@pytest.mark.parametrize("L,ctx,ps,causal,D", [
+    (512, (512, 600), 128, True, 128),
+    (700, (700, 1337), 64, True, 128),
+    (777, (800, 2000), 16, True, 128),
+    (530, (530, 531), 5, True, 128),
+    (600, (650, 1200), 32, False, 128),
+    (1000, (1000, 1100), 64, True, 64),
+])
+def test_prefill_long_queries(L, ctx, ps, causal, D):
+    p = small(120 + L + ps, B=2, Hq=4, Hkv=2, L=L, ctx=ctx, ps=ps, causal=causal, poison=True, D=D)
+    say(f"long query L={L} ctx={ctx} ps={ps} causal={causal} D={D}")
+    parity(run_gpu(p), ref(p), f"long query L={L} ps={ps}")
+
+
 def test_noncausal_prefill():
     p = small(95, B=2, Hq=4, Hkv=4, L=70, ctx=(30, 200), ps=16, causal=False, poison=True)
     parity(run_gpu(p), ref(p), "noncausal prefill")
