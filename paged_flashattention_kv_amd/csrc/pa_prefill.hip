@@ -161,11 +161,28 @@ __device__ __forceinline__ void lookup_tile(const PrefillArgs& a, const int32_t*
 // [16w, 16w + 16) of the tile: instruction i covers the kRowsPerInst keys
 // from 16w + kRowsPerInst*i; lane l takes key 16w + kRowsPerInst*i + l/kChunks
 // and LDS chunk position l % kChunks, which holds global chunk
-// (l % kChunks) ^ swz(key).
+// (l % kChunks) ^ swz(key). A whole aligned tile is one contiguous span of
+// one page: a wave-uniform base (scalar registers) plus a per-lane byte
+// offset that is the same for every tile, so its loads cost no vector
+// arithmetic.
 template <bool ALIGNED, int D>
 __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages<ALIGNED, D>& tp, int ctx, int t0,
                                            int wave, int lane, char* kbuf, char* vbuf) {
   using T = Tile<D>;
+  if (ALIGNED && t0 + kBN <= ctx) {
+    const char* kbase = reinterpret_cast<const char*>(a.kpages + tp.row[0]);
+    const char* vbase = reinterpret_cast<const char*>(a.vpages + tp.row[0]);
+#pragma unroll
+    for (int i = 0; i < T::kInsts; ++i) {
+      const int key = 16 * wave + T::kRowsPerInst * i + lane / T::kChunks;  // key inside the tile
+      const int chunk = (lane % T::kChunks) ^ swz<D>(key);
+      const uint32_t off = (uint32_t)(key * D + chunk * 8) * 2u;  // bytes from the tile's first row
+      const int lds_off = wave * 32 * D + i * 1024;
+      __builtin_amdgcn_global_load_lds((global_void*)(kbase + off), (lds_void*)(kbuf + lds_off), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void*)(vbase + off), (lds_void*)(vbuf + lds_off), 16, 0, 0);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < T::kInsts; ++i) {
     const int key = 16 * wave + T::kRowsPerInst * i + lane / T::kChunks;  // key inside the tile
@@ -184,6 +201,29 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages
   }
 }
 
+// 32-bit LDS address of a pointer into a __shared__ buffer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// ds_read_b128 issued as written (the compiler neither moves nor waits for
+// it): the caller waits with lds_wait before using the result. Other LDS
+// reads in flight only make such a counted wait longer, never too short.
+template <int kOff>
+__device__ __forceinline__ void lds_read_b128(u32x4_t& dst, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(kOff));
+}
+
+// Waits until at most n LDS reads are in flight; the fragments pass through
+// the statement so that their users come after the wait.
+__device__ __forceinline__ void lds_wait(int n, u32x4_t (&f)[2]) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f[0]), "+v"(f[1])); break;
+    case 2: asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(f[0]), "+v"(f[1])); break;
+    default: asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(f[0]), "+v"(f[1])); break;
+  }
+}
+
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <bool ALIGNED, int D, bool MASKED>
@@ -196,7 +236,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar address math
   const int half = lane >> 5;  // which 8-wide k slice of an MFMA operand this lane feeds
   const int col = lane & 31;   // query row (within the wave) owned by this lane
 
@@ -323,22 +363,47 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
       }
     }
     if (t + 1 < n_tiles) issue_tile<ALIGNED, D>(a, tp, ctx, t0 + kBN, wave, lane, knext, vnext);
-    // lookup for tile t + 2 (clamped so that it is unconditional)
-    lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, min(t + 2, n_tiles - 1) * kBN, wave, lane, tp);
-    if (!active) return;
+    // Lookup for tile t + 2 (clamped so that it is unconditional), done
+    // after this tile's matrix work, not between the barrier and it.
+    const int t_look = min(t + 2, n_tiles - 1) * kBN;
+    if (!active) {
+      lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, t_look, wave, lane, tp);
+      return;
+    }
 
       // ---- S^T = K Q^T : two 32-key blocks ----
+      // Contraction step ks runs the MFMAs of both blocks; the K fragments of
+      // step ks + 2 are read from LDS meanwhile. The reads and their waits
+      // are explicit: LDS reads complete in order, so before step ks only
+      // the reads of the two later steps may still be in flight.
       f32x16_t acc_s[2];
   #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
   #pragma unroll
         for (int i = 0; i < 16; ++i) acc_s[kb][i] = 0.f;
-        const int key = 32 * kb + col;
+      {
+        // Chunk 2ks + half of key col (block 0) and key 32 + col (block 1).
+        // Chunk positions are XOR-swizzled and the chunk bits of a row's
+        // byte offset are zero, so step ks is an XOR by 2ks chunks.
+        const uint32_t kaddr0 = lds_addr(kb_base) + tile_off<D>(col, half);
+        u32x4_t kf[3][2];  // [buffer][block]
+        auto read_k = [&](int ks, u32x4_t (&dst)[2]) {
+          const uint32_t a0 = kaddr0 ^ (uint32_t)(ks << 5);
+          lds_read_b128<0>(dst[0], a0);
+          lds_read_b128<32 * 2 * D>(dst[1], a0);
+        };
+        read_k(0, kf[0]);
+        read_k(1, kf[1]);
   #pragma unroll
         for (int ks = 0; ks < T::kKs; ++ks) {
-          const bf16x8_t kfrag = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4_t*>(kb_base + tile_off<D>(key, 2 * ks + half)));
-          acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qv[ks], acc_s[kb], 0, 0, 0);
+          if (ks + 2 < T::kKs) read_k(ks + 2, kf[(ks + 2) % 3]);
+          const int younger = 2 * min(2, T::kKs - 1 - ks);  // reads issued after step ks's
+          lds_wait(younger, kf[ks % 3]);
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[ks % 3][kb]), qv[ks],
+                                                                acc_s[kb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
 
@@ -429,6 +494,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
           acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pfrag, acc_o[db], 0, 0, 0);
         }
       }
+      lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, t_look, wave, lane, tp);
   };
   for (int t = 0; t < n_tiles; t += 2) {
     tile_step(t, lds_k0, lds_v0, lds_k1, lds_v1);
