@@ -224,6 +224,49 @@ __device__ __forceinline__ void lds_wait(int n, u32x4_t (&f)[2]) {
   }
 }
 
+// Waits until at most n LDS reads are in flight (n a compile-time constant
+// after unrolling); the fragment passes through the statement so that its
+// users come after the wait.
+__device__ __forceinline__ void lds_wait_n(int n, u32x4_t& f) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f)); break;
+    case 1: asm volatile("s_waitcnt lgkmcnt(1)" : "+v"(f)); break;
+    case 2: asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(f)); break;
+    case 3: asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(f)); break;
+    case 4: asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(f)); break;
+    case 5: asm volatile("s_waitcnt lgkmcnt(5)" : "+v"(f)); break;
+    default: asm volatile("s_waitcnt lgkmcnt(6)" : "+v"(f)); break;
+  }
+}
+
+// The two transposed 8-byte reads of one V^T fragment (ds_read_b64_tr_b16:
+// lane i of each 16-lane group receives element i % 4 of the 8 bytes that
+// lane 4j + i / 4 addresses, as its element j) for 16-key step ks of the
+// tile, issued as written.
+template <int kStepBytes>
+__device__ __forceinline__ void lds_read_tr_pair(u32x4_t& f, uint32_t lo_addr, uint32_t hi_addr, int ks) {
+  u32x2_t lo, hi;
+  switch (ks) {
+    case 0:
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(lo_addr));
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(hi_addr));
+      break;
+    case 1:
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(lo_addr), "i"(kStepBytes));
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(hi_addr), "i"(kStepBytes));
+      break;
+    case 2:
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(lo_addr), "i"(2 * kStepBytes));
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(hi_addr), "i"(2 * kStepBytes));
+      break;
+    default:
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(lo_addr), "i"(3 * kStepBytes));
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(hi_addr), "i"(3 * kStepBytes));
+      break;
+  }
+  f = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+}
+
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <bool ALIGNED, int D, bool MASKED>
@@ -323,6 +366,12 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   const int vc_lane = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int vb_lane = 8 * (lane & 1);
   const uint32_t ones_bf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
+  // V^T fragment of 16-key step 0, dims [0, 32): rows vk_lane and vk_lane + 8,
+  // chunk vc_lane, byte vb_lane. Chunk positions are XOR-swizzled and the
+  // chunk bits of a row offset are zero, so dims block db is an XOR by 4db
+  // chunks and step ks adds 16 rows.
+  const uint32_t v_lane0 = (uint32_t)tile_off<D>(vk_lane, vc_lane) + vb_lane;
+  const uint32_t v_lane1 = (uint32_t)tile_off<D>(vk_lane + 8, vc_lane) + vb_lane;
 
   const int row_abs = r0 + col;
   // this lane's mask row (MASKED only; rows past L read row L - 1, never stored)
@@ -407,6 +456,19 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
         }
       }
 
+      // V^T fragments of the first kVA P V groups: read during the softmax
+      constexpr int kVG = 4 * T::kDb;  // P V groups: (16-key step, 32-dim block)
+      constexpr int kVA = 3;           // groups read ahead
+      const uint32_t vaddr0 = lds_addr(vb_base) + v_lane0, vaddr1 = lds_addr(vb_base) + v_lane1;
+      u32x4_t vf[kVA + 1];
+      auto issue_v = [&](int g) {
+        if (g >= kVG) return;
+        const int ks = g / T::kDb, db = g % T::kDb;
+        lds_read_tr_pair<16 * 2 * D>(vf[g % (kVA + 1)], vaddr0 ^ (uint32_t)(db << 6), vaddr1 ^ (uint32_t)(db << 6), ks);
+      };
+  #pragma unroll
+      for (int g = 0; g < kVA; ++g) issue_v(g);
+
       // ---- mask, online softmax (row = this lane's query row) ----
       // element i of block kb is key 32kb + 8(i/4) + 4half + i%4 of the tile.
       // Without an explicit mask the maximum is taken on raw scores (c > 0)
@@ -474,25 +536,18 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
       }
       l_run += psum;
 
-      // ---- O^T += V^T P^T : 4 blocks of 32 dims, 4 steps of 16 keys ----
+      // ---- O^T += V^T P^T : 4 steps of 16 keys, 32-dim blocks ----
+      // LDS reads complete in order: before group g only the reads of the
+      // next kVA groups may still be in flight.
   #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int g = 0; g < kVG; ++g) {
+        const int ks = g / T::kDb, db = g % T::kDb;
+        issue_v(g + kVA);
+        lds_wait_n(2 * min(kVA, kVG - 1 - g), vf[g % (kVA + 1)]);
         const uint32_t* src = &pk[ks >> 1][(ks & 1) * 4];
         const u32x4_t pw = {src[0], src[1], src[2], src[3]};
-        const bf16x8_t pfrag = __builtin_bit_cast(bf16x8_t, pw);
-        const int key0 = 16 * ks + vk_lane;
-  #pragma unroll
-        for (int db = 0; db < T::kDb; ++db) {
-          const int c = 4 * db + vc_lane;
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(vb_base + tile_off<D>(key0, c) + vb_lane));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(vb_base + tile_off<D>(key0 + 8, c) + vb_lane));
-          const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
-          const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
-          const u32x4_t vw = {lw.x, lw.y, hw.x, hw.y};
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pfrag, acc_o[db], 0, 0, 0);
-        }
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[g % (kVA + 1)]),
+                                                            __builtin_bit_cast(bf16x8_t, pw), acc_o[db], 0, 0, 0);
       }
       lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, t_look, wave, lane, tp);
   };
