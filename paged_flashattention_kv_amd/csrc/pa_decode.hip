@@ -78,6 +78,7 @@ struct Geo {
 // by more than kTau (log2 units), so weights stay <= 2^kTau and the common
 // case needs no rescale of the accumulators.
 constexpr float kTau = 8.0f;
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
 constexpr int kGran = 64;    // keys per granule: work ranges start and end on granules
 constexpr int kWindow = 2048;  // keys per block-table staging window
@@ -238,8 +239,12 @@ __device__ __forceinline__ void compute_stage(const Stage& st, const float (&mv)
         if (!(key < s1 && key <= last[r])) s[r][i] = -INFINITY;
     }
   }
-  // online softmax: the step maximum moves the reference only past the threshold
-  float p[ROWS][kTK];
+  // online softmax: the step maximum moves the reference only past the
+  // threshold. The weights of keys (2i, 2i + 1) are packed as a bf16 pair:
+  // P V below runs on packed bf16 dot products, and the row sum adds the same
+  // rounded weights.
+  static_assert(kTK % 2 == 0, "keys are paired for the packed weights");
+  uint32_t pp[ROWS][kTK / 2];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     float tmax = s[r][0];
@@ -254,26 +259,29 @@ __device__ __forceinline__ void compute_stage(const Stage& st, const float (&mv)
       for (int j = 0; j < 16; ++j) rs.acc[r][j] *= alpha;
     }
     const float mref = rs.m[r] == -INFINITY ? 0.f : rs.m[r];
-    float ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < kTK; ++i) {
-      p[r][i] = fast_exp2(fmaf(s[r][i], c, -mref));
-      ps += p[r][i];
+    for (int i = 0; i < kTK / 2; ++i) {
+      pp[r][i] = pack_bf16x2(fast_exp2(fmaf(s[r][2 * i], c, -mref)), fast_exp2(fmaf(s[r][2 * i + 1], c, -mref)));
+      rs.lsum[r] = dot2_bf16(pp[r][i], kOnesBf16x2, rs.lsum[r]);
     }
-    rs.lsum[r] += ps;
   }
-  // weighted values, fp32
+  // weighted values: for each pair of keys and each pair of dims, the two
+  // keys' values of one dim are gathered into a bf16 pair (v_perm_b32) and
+  // dotted with the pair of weights, accumulating in fp32
 #pragma unroll
-  for (int i = 0; i < kTK; ++i) {
-    const uint32_t w[8] = {st.v[i][0].x, st.v[i][0].y, st.v[i][0].z, st.v[i][0].w,
-                           st.v[i][1].x, st.v[i][1].y, st.v[i][1].z, st.v[i][1].w};
+  for (int i = 0; i < kTK / 2; ++i) {
+    const uint32_t w0[8] = {st.v[2 * i][0].x, st.v[2 * i][0].y, st.v[2 * i][0].z, st.v[2 * i][0].w,
+                            st.v[2 * i][1].x, st.v[2 * i][1].y, st.v[2 * i][1].z, st.v[2 * i][1].w};
+    const uint32_t w1[8] = {st.v[2 * i + 1][0].x, st.v[2 * i + 1][0].y, st.v[2 * i + 1][0].z, st.v[2 * i + 1][0].w,
+                            st.v[2 * i + 1][1].x, st.v[2 * i + 1][1].y, st.v[2 * i + 1][1].z, st.v[2 * i + 1][1].w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+      const uint32_t lo = __builtin_amdgcn_perm(w1[j], w0[j], 0x05040100u);  // dim 2j of both keys
+      const uint32_t hi = __builtin_amdgcn_perm(w1[j], w0[j], 0x07060302u);  // dim 2j + 1 of both keys
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
-        rs.acc[r][2 * j] = fmaf(p[r][i], lo, rs.acc[r][2 * j]);
-        rs.acc[r][2 * j + 1] = fmaf(p[r][i], hi, rs.acc[r][2 * j + 1]);
+        rs.acc[r][2 * j] = dot2_bf16(pp[r][i], lo, rs.acc[r][2 * j]);
+        rs.acc[r][2 * j + 1] = dot2_bf16(pp[r][i], hi, rs.acc[r][2 * j + 1]);
       }
     }
   }
