@@ -287,16 +287,6 @@ __device__ __forceinline__ void compute_stage(const Stage& st, const float (&mv)
   }
 }
 
-// Device-coherent (agent scope, relaxed) accesses of the partial states.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Wait until this wave's memory operations (stores included) have completed.
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 __device__ __forceinline__ int64_t n_gran(int ctx) { return ctx > 0 ? (ctx + kGran - 1) / kGran : 0; }
 
 // Query rows of sequence b that this launch serves (0: none), and for a
@@ -492,28 +482,6 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
         store_coherent(a.ws_ml + (part + r) * 2 + 1, den);
       }
     }
-  }
-}
-
-// Arrival at a shared segment's counter; true for the last of n arrivals.
-// The counter word holds (epoch << 32 | arrivals so far); a word tagged with
-// another epoch (an earlier call) counts as zero. The last arrival resets
-// the word to 0.
-//
-// Ordering without cache-wide fences (an agent-scope fence writes back and
-// invalidates a whole XCD L2 here): partials are written with device-coherent
-// stores; every wave waits for its stores to complete (vmcnt(0)) before the
-// work item's barrier, and only then is the counter updated. The last
-// arrival reads the partials with device-coherent loads issued after it has
-// seen the final count.
-__device__ __forceinline__ bool arrive_last(uint64_t* ctr, uint32_t epoch, uint32_t n) {
-  uint64_t v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (;;) {
-    const uint32_t cnt = (uint32_t)(v >> 32) == epoch ? (uint32_t)v : 0u;
-    const uint64_t nv = cnt + 1 == n ? 0ull : ((uint64_t)epoch << 32 | (cnt + 1));
-    if (__hip_atomic_compare_exchange_strong(ctr, &v, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT))
-      return cnt + 1 == n;
   }
 }
 

@@ -100,4 +100,67 @@ __device__ __forceinline__ float sum_stride(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- partial states shared between work items (split-range merges) ----
+
+// Device-coherent (agent scope, relaxed) accesses of partial states.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 8- and 16-byte device-coherent stores and loads (the same cache policy as
+// the relaxed agent-scope accesses above). The loads are issued as written
+// and not tracked by the compiler: wait_loads_x waits for them.
+__device__ __forceinline__ void store_coherent_x2(float* p, f32x2_t v) {
+  asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_coherent_x4(float* p, f32x4_t v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ f32x2_t load_coherent_x2(const float* p) {
+  f32x2_t v;
+  asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ f32x4_t load_coherent_x4(const float* p) {
+  f32x4_t v;
+  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+// Waits for every vector memory operation of the wave; the loaded values
+// pass through the statement so that their uses come after the wait.
+template <int P, int S>
+__device__ __forceinline__ void wait_loads_x(f32x2_t (&a)[P][S], f32x4_t (&b)[P][S]) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < P; ++i)
+#pragma unroll
+    for (int j = 0; j < S; ++j) asm volatile("" : "+v"(a[i][j]), "+v"(b[i][j]));
+}
+// Wait until this wave's memory operations (stores included) have completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Arrival at a counter shared by n work items; true for the last of the n
+// arrivals. The counter word holds (epoch << 32 | arrivals so far); a word
+// tagged with another epoch (an earlier call) counts as zero. The last
+// arrival resets the word to 0.
+//
+// Ordering without cache-wide fences (an agent-scope fence writes back and
+// invalidates a whole XCD L2 here): partials are written with device-coherent
+// stores; every wave waits for its stores to complete (vmcnt(0)) before the
+// work item's barrier, and only then is the counter updated. The last
+// arrival reads the partials with device-coherent loads issued after it has
+// seen the final count.
+__device__ __forceinline__ bool arrive_last(uint64_t* ctr, uint32_t epoch, uint32_t n) {
+  uint64_t v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    const uint32_t cnt = (uint32_t)(v >> 32) == epoch ? (uint32_t)v : 0u;
+    const uint64_t nv = cnt + 1 == n ? 0ull : ((uint64_t)epoch << 32 | (cnt + 1));
+    if (__hip_atomic_compare_exchange_strong(ctr, &v, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return cnt + 1 == n;
+  }
+}
+
 }  // namespace pa

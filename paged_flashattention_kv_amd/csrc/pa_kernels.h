@@ -21,7 +21,7 @@ struct KernelArgs {
   int head_dim = 128;  // 64, 128 or 256
   float scale;
   int causal;
-  uint32_t epoch;  // per-call tag of the decode arrival counters (never 0)
+  uint32_t epoch;  // per-call tag of the arrival counters in the workspace (never 0)
   // Mixed batch: query and out are packed token-major [total_query, H_q, D]
   // and sequence b owns tokens [query_start[b], query_start[b + 1]);
   // query_len is then the longest query of the batch. The decode launch

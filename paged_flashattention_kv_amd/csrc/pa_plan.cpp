@@ -80,6 +80,18 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
     p.aligned = s.page_size % kPrefillBlockN == 0;
     p.num_work = int64_t(p.n_qtiles) * s.num_q_heads * s.batch;
     if (p.num_work > INT32_MAX) return fail(err, kErrUnsupported, "prefill grid too large");
+    if (p.num_work < kPrefillSplitTarget) {
+      int64_t splits = std::min<int64_t>(kPrefillMaxSplits, kPrefillSplitTarget / p.num_work);
+      splits = std::min<int64_t>(splits, max_ctx / (2 * kPrefillBlockN));  // two tiles per part at least
+      p.kv_splits = int(std::max<int64_t>(splits, 1));
+    }
+    if (p.kv_splits > 1) {
+      const size_t parts = size_t(p.num_work) * size_t(p.kv_splits) * kPrefillBlockM;
+      p.ws_ctr_offset = 0;
+      p.ws_ml_offset = align_up(size_t(p.num_work) * sizeof(uint64_t), 256);
+      p.ws_acc_offset = align_up(p.ws_ml_offset + parts * 2 * sizeof(float), 256);
+      p.workspace_bytes = align_up(p.ws_acc_offset + parts * size_t(s.head_dim) * sizeof(float), 256);
+    }
   }
   *plan = p;
   if (err) err->clear();
@@ -122,6 +134,10 @@ int make_plan_varlen(const Shape& s, int decode_max_len, int decode_work_items, 
   if (s.query_len > v.dec_max_len) {
     v.pre = probe;
     v.run_prefill = true;
+    if (v.pre.kv_splits > 1) {
+      v.pre_ws_offset = align_up(v.workspace_bytes, 256);
+      v.workspace_bytes = v.pre_ws_offset + v.pre.workspace_bytes;
+    }
   }
   *plan = v;
   if (err) err->clear();

@@ -21,6 +21,12 @@ constexpr int kDecodeAutoCap = 2048; // most decode work items the automatic cho
 constexpr int kDecodeMaxWork = 65536;
 constexpr int kPrefillBlockM = 128;  // query rows per prefill work item
 constexpr int kPrefillBlockN = 64;   // keys per prefill K/V tile
+// A prefill launch with fewer work items than kPrefillSplitTarget (two per CU
+// on a 256-CU part) splits every work item's key range into up to
+// kPrefillMaxSplits parts of at least two tiles each, merged through the
+// workspace.
+constexpr int kPrefillSplitTarget = 512;
+constexpr int kPrefillMaxSplits = 4;
 constexpr int kScheduleDecode = 1;
 constexpr int kSchedulePrefill = 2;
 
@@ -40,14 +46,20 @@ struct Plan {
   int work_cap = 0;        // decode: most work items the workspace is sized for
   int bt_entries = 0;      // decode: block-table entries staged per window
   int n_qtiles = 0;        // prefill: query tiles per (sequence, head)
+  int kv_splits = 1;       // prefill: parts of each work item's key range (1: no split)
   int ps_log2 = -1;        // log2(page_size) or -1 if not a power of two
   bool aligned = false;    // every tile lies inside one page
   int64_t max_ctx = 0;     // max_pages * page_size
   int64_t num_work = 0;    // work items (workgroups) of the main kernel
   size_t workspace_bytes = 0;
-  size_t ws_ctr_offset = 0;   // decode arrival counters [B * H_kv] u64 (zero-filled before first use)
-  size_t ws_ml_offset = 0;    // decode partial (max, sum) [work_cap][2][rows][2] f32
-  size_t ws_acc_offset = 0;   // decode partial outputs    [work_cap][2][rows][D] f32
+  // decode: arrival counters [B * H_kv] u64 (zero-filled before first use),
+  // partial (max, sum) [work_cap][2][rows][2] f32, partial outputs
+  // [work_cap][2][rows][D] f32. Split prefill: counters [num_work] u64,
+  // (max, sum) [num_work][kv_splits][128][2] f32, outputs
+  // [num_work][kv_splits][128][D] f32.
+  size_t ws_ctr_offset = 0;
+  size_t ws_ml_offset = 0;
+  size_t ws_acc_offset = 0;
 };
 
 // Error codes (the same values as the PA_ERR_* codes of the C header).
@@ -65,6 +77,7 @@ struct VarlenPlan {
   bool run_prefill = false;
   Plan dec;  // decode part: rows = group * dec_max_len (the workspace slot stride)
   Plan pre;  // prefill part: query tiles cover max_query_len
+  size_t pre_ws_offset = 0;  // the prefill part's workspace (key-range split) follows the decode part's
   size_t workspace_bytes = 0;
 };
 

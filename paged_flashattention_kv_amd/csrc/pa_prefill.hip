@@ -104,6 +104,15 @@ struct PrefillArgs {
   int64_t msb, msh, msl;
   int mask_len;
   int mask_vec;  // every mask row starts 16-byte aligned: four keys per load
+  // Split key range: work item i's part s (s < kv_splits) covers tiles
+  // [s * n / kv_splits, (s + 1) * n / kv_splits) of its n tiles and leaves
+  // its rows' (reference max, row sum, unnormalised output) in slot
+  // i * kv_splits + s; the part that arrives last at counter i merges them.
+  int num_work, kv_splits;
+  uint64_t* ws_ctr;  // [num_work] arrival counters (epoch << 32 | count)
+  float* ws_ml;      // [num_work * kv_splits][128][2]
+  float* ws_acc;     // [num_work * kv_splits][128][D]
+  uint32_t epoch;
 };
 
 __device__ __forceinline__ int div_ps(int s, int ps, int ps_log2) { return ps_log2 >= 0 ? (s >> ps_log2) : s / ps; }
@@ -284,12 +293,15 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   const int col = lane & 31;   // query row (within the wave) owned by this lane
 
   // ---- work item: heavy query tiles first, GQA siblings together on one XCD ----
-  const int n = gridDim.x;
-  int logical = blockIdx.x;
+  // Workgroup w runs part w / num_work of work item w % num_work.
+  const int n = a.num_work;
+  const int item = (int)(blockIdx.x % (unsigned)n);
+  const int part = (int)(blockIdx.x / (unsigned)n);
+  int logical = item;
   const int G = a.group;
   if (n % (8 * G) == 0) {
-    const int xcd = blockIdx.x & 7;
-    const int k = blockIdx.x >> 3;
+    const int xcd = item & 7;  // the XCD of workgroup w is w % 8, and n is a multiple of 8
+    const int k = item >> 3;
     logical = ((k / G) * 8 + xcd) * G + (k % G);
   }
   const int g = logical % G;
@@ -314,7 +326,10 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   const int offset = ctx - L;  // query row l sits at logical position l + offset
   const int tile_last_row = min(q0 + kBM, L) - 1;
   const int kv_end = a.causal ? min(ctx, tile_last_row + offset + 1) : ctx;
-  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  const int n_tiles_all = (kv_end + kBN - 1) / kBN;
+  // this workgroup's tiles [t_lo, n_tiles)
+  const int t_lo = (int)((int64_t)part * n_tiles_all / a.kv_splits);
+  const int n_tiles = (int)((int64_t)(part + 1) * n_tiles_all / a.kv_splits);
 
   const int r0 = q0 + 32 * wave;  // first query row of this wave
   const bool wave_has_rows = r0 < L;
@@ -328,10 +343,10 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
 
   // ---- first tile in flight before anything else ----
   TilePages<ALIGNED, D> tp;
-  if (n_tiles > 0) {
-    lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, 0, wave, lane, tp);
-    issue_tile<ALIGNED, D>(a, tp, ctx, 0, wave, lane, lds_k0, lds_v0);
-    lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, min(1, n_tiles - 1) * kBN, wave, lane, tp);
+  if (n_tiles > t_lo) {
+    lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, t_lo * kBN, wave, lane, tp);
+    issue_tile<ALIGNED, D>(a, tp, ctx, t_lo * kBN, wave, lane, lds_k0, lds_v0);
+    lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, min(t_lo + 1, n_tiles - 1) * kBN, wave, lane, tp);
   }
 
   // ---- Q^T operand: lane holds row r0 + col, dims 16ks + 8half .. +8 ----
@@ -551,38 +566,121 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
       }
       lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, t_look, wave, lane, tp);
   };
-  for (int t = 0; t < n_tiles; t += 2) {
+  for (int t = t_lo; t < n_tiles; t += 2) {
     tile_step(t, lds_k0, lds_v0, lds_k1, lds_v1);
     if (t + 1 < n_tiles) tile_step(t + 1, lds_k1, lds_v1, lds_k0, lds_v0);
   }
   wait_all_loads();  // no load may still be writing this work item's LDS at exit
 
   // ---- finalize: divide by the row sum, store bf16 ----
-  if (!wave_has_rows) return;
-  const float l_tot = sum_xor32(l_run);
-  if (row_abs >= L) return;
-  const float inv = 1.f / l_tot;
-  const size_t orow = a.qstart ? (size_t)(start + row_abs) * a.num_q_heads + head
-                               : ((size_t)b * a.num_q_heads + head) * L + row_abs;
-  uint16_t* op = a.out + orow * D;
+  if (a.kv_splits == 1) {
+    if (!wave_has_rows) return;
+    const float l_tot = sum_xor32(l_run);
+    if (row_abs >= L) return;
+    const float inv = 1.f / l_tot;
+    const size_t orow = a.qstart ? (size_t)(start + row_abs) * a.num_q_heads + head
+                                 : ((size_t)b * a.num_q_heads + head) * L + row_abs;
+    uint16_t* op = a.out + orow * D;
 #pragma unroll
-  for (int db = 0; db < T::kDb; ++db) {
+    for (int db = 0; db < T::kDb; ++db) {
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      const int d0 = 32 * db + 8 * grp + 4 * half;
-      const u32x2_t w = {pack_bf16x2(acc_o[db][4 * grp] * inv, acc_o[db][4 * grp + 1] * inv),
-                         pack_bf16x2(acc_o[db][4 * grp + 2] * inv, acc_o[db][4 * grp + 3] * inv)};
-      *reinterpret_cast<u32x2_t*>(op + d0) = w;
+      for (int grp = 0; grp < 4; ++grp) {
+        const int d0 = 32 * db + 8 * grp + 4 * half;
+        const u32x2_t w = {pack_bf16x2(acc_o[db][4 * grp] * inv, acc_o[db][4 * grp + 1] * inv),
+                           pack_bf16x2(acc_o[db][4 * grp + 2] * inv, acc_o[db][4 * grp + 3] * inv)};
+        *reinterpret_cast<u32x2_t*>(op + d0) = w;
+      }
+    }
+    return;
+  }
+
+  // ---- split key range: leave this part's state, the last part merges ----
+  // (the reference is wave-uniform per row: m_run of this lane's row; a row
+  // that saw no key keeps -inf, sum 0 and a zero output). Device-coherent
+  // 16-byte stores: lane (col, half) holds dims 32db + 8g + 4half .. +4.
+  const size_t slot = (size_t)item * a.kv_splits + part;
+  if (wave_has_rows) {
+    const float l_tot = sum_xor32(l_run);
+    if (row_abs < L) {
+      const size_t r = slot * kBM + 32 * wave + col;
+      if (half == 0) store_coherent_x2(a.ws_ml + r * 2, f32x2_t{m_run, l_tot});
+#pragma unroll
+      for (int db = 0; db < T::kDb; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          store_coherent_x4(a.ws_acc + r * D + 32 * db + 8 * g4 + 4 * half,
+                            f32x4_t{acc_o[db][4 * g4], acc_o[db][4 * g4 + 1], acc_o[db][4 * g4 + 2], acc_o[db][4 * g4 + 3]});
+    }
+  }
+  wait_stores();
+  __shared__ bool lds_last;
+  __syncthreads();
+  if (tid == 0) lds_last = arrive_last(a.ws_ctr + item, a.epoch, (uint32_t)a.kv_splits);
+  __syncthreads();
+  if (!lds_last) return;
+  // Merge the parts in order ("Week 2 Day 5", Task 2: common maximum, one
+  // factor per partial, one denominator); rows past L are not stored. A row
+  // without any visible key ends as 0 / 0, as in the unsplit path. Thread t
+  // takes 4 dims of a row, kRowsPerPass rows per pass; the loads of
+  // kMergePasses passes are in flight together.
+  constexpr int kThrPerRow = D / 4;
+  constexpr int kRowsPerPass = kThreads / kThrPerRow;
+  constexpr int kMergePasses = 2;
+  const int rows_here = min(kBM, L - q0);
+  const size_t slot0 = (size_t)item * a.kv_splits;
+  const int d4 = 4 * (tid % kThrPerRow);
+  for (int r0p = 0; r0p < rows_here; r0p += kRowsPerPass * kMergePasses) {
+    for (int s0 = 0; s0 < a.kv_splits; s0 += kPrefillMaxSplits) {  // kv_splits <= kPrefillMaxSplits: one round
+      f32x2_t ml[kMergePasses][kPrefillMaxSplits];
+      f32x4_t av[kMergePasses][kPrefillMaxSplits];
+#pragma unroll
+      for (int ps = 0; ps < kMergePasses; ++ps) {
+        const int r = min(r0p + ps * kRowsPerPass + tid / kThrPerRow, rows_here - 1);  // re-read a valid row
+#pragma unroll
+        for (int s = 0; s < kPrefillMaxSplits; ++s) {
+          const size_t rr = (slot0 + min(s, a.kv_splits - 1)) * kBM + r;
+          ml[ps][s] = load_coherent_x2(a.ws_ml + rr * 2);
+          av[ps][s] = load_coherent_x4(a.ws_acc + rr * D + d4);
+        }
+      }
+      wait_loads_x(ml, av);
+#pragma unroll
+      for (int ps = 0; ps < kMergePasses; ++ps) {
+        const int r = r0p + ps * kRowsPerPass + tid / kThrPerRow;
+        if (r >= rows_here) continue;
+        float M = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < kPrefillMaxSplits; ++s)
+          if (s < a.kv_splits) M = fmaxf(M, ml[ps][s].x);
+        float den = 0.f;
+        f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kPrefillMaxSplits; ++s) {
+          if (s >= a.kv_splits) continue;
+          const float f = ml[ps][s].x == -INFINITY ? 0.f : fast_exp2(ml[ps][s].x - M);
+          den = fmaf(f, ml[ps][s].y, den);
+          num.x = fmaf(f, av[ps][s].x, num.x);
+          num.y = fmaf(f, av[ps][s].y, num.y);
+          num.z = fmaf(f, av[ps][s].z, num.z);
+          num.w = fmaf(f, av[ps][s].w, num.w);
+        }
+        const int row = q0 + r;
+        const size_t orow =
+            a.qstart ? (size_t)(start + row) * a.num_q_heads + head : ((size_t)b * a.num_q_heads + head) * L + row;
+        const u32x2_t w = {pack_bf16x2(num.x / den, num.y / den), pack_bf16x2(num.z / den, num.w / den)};
+        *reinterpret_cast<u32x2_t*>(a.out + orow * D + d4) = w;
+      }
     }
   }
 }
 
 template <int D, bool MASKED>
 hipError_t launch_mask(const PrefillArgs& a, const Plan& p, hipStream_t stream) {
+  const unsigned grid = (unsigned)(p.num_work * a.kv_splits);
   if (p.aligned)
-    hipLaunchKernelGGL((pa_prefill_mfma<true, D, MASKED>), dim3((unsigned)p.num_work), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((pa_prefill_mfma<true, D, MASKED>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((pa_prefill_mfma<false, D, MASKED>), dim3((unsigned)p.num_work), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((pa_prefill_mfma<false, D, MASKED>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -622,6 +720,17 @@ hipError_t launch_prefill(const KernelArgs& k, const Plan& p, hipStream_t stream
   a.mask_len = k.mask_len;
   a.mask_vec = k.mask && (reinterpret_cast<uintptr_t>(k.mask) % 16 == 0) && k.mask_stride_b % 4 == 0 &&
                k.mask_stride_h % 4 == 0 && k.mask_stride_l % 4 == 0;
+  a.num_work = (int)p.num_work;
+  a.kv_splits = p.kv_splits;
+  a.epoch = k.epoch;
+  a.ws_ctr = nullptr;
+  a.ws_ml = a.ws_acc = nullptr;
+  if (p.kv_splits > 1) {
+    char* ws = static_cast<char*>(k.workspace);
+    a.ws_ctr = reinterpret_cast<uint64_t*>(ws + p.ws_ctr_offset);
+    a.ws_ml = reinterpret_cast<float*>(ws + p.ws_ml_offset);
+    a.ws_acc = reinterpret_cast<float*>(ws + p.ws_acc_offset);
+  }
   switch (k.head_dim) {
     case 64: return launch_dim<64>(a, p, stream);
     case 256: return launch_dim<256>(a, p, stream);

@@ -75,6 +75,12 @@ int run_uniform(const void* query, const void* key_pages, const void* value_page
                                  page_size, max_pages, causal != 0);
   const int rc = pa::make_plan(s, schedule, decode_work_items, true, &plan, &err);
   if (rc != pa::kOk) return set_error(rc, err);
+  if (plan.schedule == pa::kSchedulePrefill && plan.kv_splits > 1 &&
+      (workspace == nullptr || workspace_bytes < plan.workspace_bytes)) {
+    // a prefill without the workspace its key-range split needs runs unsplit
+    plan.kv_splits = 1;
+    plan.workspace_bytes = 0;
+  }
   if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
     return set_error(PA_ERR_WORKSPACE, "workspace smaller than paged_attention_workspace_bytes() = " +
                                            std::to_string(plan.workspace_bytes));
@@ -313,6 +319,12 @@ int paged_attention_varlen_ex(const void* query, const void* key_pages, const vo
     g_last_error.clear();
     return PA_OK;
   }
+  if (plan.run_prefill && plan.pre.kv_splits > 1 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes)) {
+    // a prefill part without the workspace its key-range split needs runs unsplit
+    plan.pre.kv_splits = 1;
+    plan.pre.workspace_bytes = 0;
+    plan.workspace_bytes = plan.run_decode ? plan.dec.workspace_bytes : 0;
+  }
   if (plan.workspace_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.workspace_bytes))
     return set_error(PA_ERR_WORKSPACE, "workspace smaller than paged_attention_varlen_workspace_bytes() = " +
                                            std::to_string(plan.workspace_bytes));
@@ -351,7 +363,11 @@ int paged_attention_varlen_ex(const void* query, const void* key_pages, const vo
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (plan.run_decode) e = pa::launch_decode(k, plan.dec, st);
-  if (e == hipSuccess && plan.run_prefill) e = pa::launch_prefill(k, plan.pre, st);
+  if (e == hipSuccess && plan.run_prefill) {
+    pa::KernelArgs kp = k;
+    if (plan.pre.kv_splits > 1) kp.workspace = static_cast<char*>(workspace) + plan.pre_ws_offset;
+    e = pa::launch_prefill(kp, plan.pre, st);
+  }
   if (e != hipSuccess) return set_error(PA_ERR_LAUNCH, std::string("launch failed: ") + hipGetErrorString(e));
   g_last_error.clear();
   return PA_OK;

@@ -1,5 +1,6 @@
 // Host-only checks of the planning/validation code (built with g++ and
 // AddressSanitizer/UBSan by tests/test_abi.py; no HIP involved).
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <string>
@@ -62,10 +63,34 @@ int main() {
         CHECK(p.ws_ctr_offset == 0);
         CHECK(p.bt_entries == pa::kDecodeWindow / 16 + 2);
       } else {
-        CHECK(p.n_qtiles == (L + 127) / 128 && p.workspace_bytes == 0);
+        CHECK(p.n_qtiles == (L + 127) / 128);
+        // 3 * 8G work items, fewer than 512: the key range (4800 keys) splits
+        // into as many parts as keep 512 workgroups busy, at most 4
+        const int64_t nw = int64_t(3) * 8 * G * p.n_qtiles;
+        CHECK(p.num_work == nw);
+        const int want = int(std::max<int64_t>(1, std::min<int64_t>(pa::kPrefillMaxSplits, pa::kPrefillSplitTarget / nw)));
+        CHECK(p.kv_splits == want);
+        if (want > 1) {
+          CHECK(p.ws_ctr_offset == 0 && p.ws_ml_offset >= size_t(nw) * 8 && p.ws_ml_offset % 256 == 0);
+          CHECK(p.ws_acc_offset >= p.ws_ml_offset + size_t(nw) * want * 128 * 2 * 4 && p.ws_acc_offset % 256 == 0);
+          CHECK(p.workspace_bytes >= p.ws_acc_offset + size_t(nw) * want * 128 * 128 * 4);
+        } else {
+          CHECK(p.workspace_bytes == 0);
+        }
       }
     }
   }
+  // key-range splits: at least two 64-key tiles per part, none from 512 work items up
+  CHECK(pa::make_plan(shape(1, 4, 2, 13, 128, 4, 4), 0, 0, true, &p, &err) == pa::kOk);
+  CHECK(p.schedule == pa::kSchedulePrefill && p.kv_splits == 1 && p.workspace_bytes == 0);
+  CHECK(pa::make_plan(shape(1, 4, 2, 150, 128, 64, 3), 0, 0, true, &p, &err) == pa::kOk);
+  CHECK(p.num_work == 8 && p.kv_splits == 1);  // 192 keys: one part of two tiles at most
+  CHECK(pa::make_plan(shape(1, 4, 2, 150, 128, 64, 4), 0, 0, true, &p, &err) == pa::kOk);
+  CHECK(p.kv_splits == 2 && p.workspace_bytes > 0);
+  CHECK(pa::make_plan(shape(8, 32, 8, 65, 128, 128, 29), 0, 0, true, &p, &err) == pa::kOk);
+  CHECK(p.num_work == 256 && p.kv_splits == 2);  // the chunked continuation
+  CHECK(pa::make_plan(shape(2, 128, 8, 256, 128, 128, 16), 0, 0, true, &p, &err) == pa::kOk);
+  CHECK(p.num_work == 512 && p.kv_splits == 1 && p.workspace_bytes == 0);
   // the five measured shapes
   CHECK(pa::make_plan(shape(64, 32, 8, 1, 128, 128, 33), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(p.schedule == pa::kScheduleDecode && p.aligned && p.rows == 4);
@@ -95,17 +120,26 @@ int main() {
       const int want = G * maxL <= 8 ? maxL : (G <= 8 ? 1 : 0);
       CHECK(v.dec_max_len == want);
       CHECK(v.run_decode == (want > 0) && v.run_prefill == (maxL > want));
+      const size_t dec_ws = v.run_decode ? v.dec.workspace_bytes : 0;
       if (v.run_decode) {
         CHECK(v.dec.schedule == pa::kScheduleDecode && v.dec.rows == G * want && v.dec.rows_pad <= 8);
-        CHECK(v.workspace_bytes == v.dec.workspace_bytes && v.workspace_bytes > 0);
-      } else {
-        CHECK(v.workspace_bytes == 0);
+        CHECK(dec_ws > 0);
       }
-      if (v.run_prefill) CHECK(v.pre.schedule == pa::kSchedulePrefill && v.pre.n_qtiles == (maxL + 127) / 128);
+      if (v.run_prefill) {
+        CHECK(v.pre.schedule == pa::kSchedulePrefill && v.pre.n_qtiles == (maxL + 127) / 128);
+        if (v.pre.kv_splits > 1) {
+          CHECK(v.pre_ws_offset >= dec_ws && v.pre_ws_offset % 256 == 0);
+          CHECK(v.workspace_bytes == v.pre_ws_offset + v.pre.workspace_bytes);
+        } else {
+          CHECK(v.workspace_bytes == dec_ws);
+        }
+      } else {
+        CHECK(v.workspace_bytes == dec_ws);
+      }
     }
   }
   CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 128, 128, 9), 0, 0, true, &v, &err) == pa::kOk);
-  CHECK(!v.run_decode && v.run_prefill && v.dec_max_len == 0 && v.workspace_bytes == 0);
+  CHECK(!v.run_decode && v.run_prefill && v.dec_max_len == 0 && v.pre.num_work == 2048 && v.workspace_bytes == 0);
   CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 128, 128, 9), 1, 0, true, &v, &err) == pa::kOk);
   CHECK(v.run_decode && v.run_prefill && v.dec_max_len == 1 && v.dec.rows == 4);
   CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 128, 128, 9), 3, 0, true, &v, &err) == pa::kErrInvalid);
