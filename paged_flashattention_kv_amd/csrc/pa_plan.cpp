@@ -76,9 +76,10 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
     p.ws_acc_offset = align_up(p.ws_ml_offset + slots * 2 * sizeof(float), 256);
     p.workspace_bytes = align_up(p.ws_acc_offset + slots * size_t(s.head_dim) * sizeof(float), 256);
   } else {
-    p.n_qtiles = int(cdiv(s.query_len, kPrefillBlockM));
+    // rows of a work item: (position, query head) pairs of one kv head's group
+    p.n_qtiles = int(cdiv(rows, kPrefillBlockM));
     p.aligned = s.page_size % kPrefillBlockN == 0;
-    p.num_work = int64_t(p.n_qtiles) * s.num_q_heads * s.batch;
+    p.num_work = int64_t(p.n_qtiles) * s.num_kv_heads * s.batch;
     if (p.num_work > INT32_MAX) return fail(err, kErrUnsupported, "prefill grid too large");
     if (p.num_work < kPrefillSplitTarget) {
       int64_t splits = std::min<int64_t>(kPrefillMaxSplits, kPrefillSplitTarget / p.num_work);

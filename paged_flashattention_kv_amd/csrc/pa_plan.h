@@ -19,7 +19,7 @@ constexpr int kDecodeMaxRows = 8;    // q rows (GQA group x query_len) per decod
 constexpr int kDecodeWindow = 2048;  // keys whose block-table entries a decode work item stages at once
 constexpr int kDecodeAutoCap = 2048; // most decode work items the automatic choice launches
 constexpr int kDecodeMaxWork = 65536;
-constexpr int kPrefillBlockM = 128;  // query rows per prefill work item
+constexpr int kPrefillBlockM = 128;  // packed (position, query head) rows per prefill work item
 constexpr int kPrefillBlockN = 64;   // keys per prefill K/V tile
 // A prefill launch with fewer work items than kPrefillSplitTarget (two per CU
 // on a 256-CU part) splits every work item's key range into up to
@@ -45,7 +45,7 @@ struct Plan {
   int work_items = 0;      // decode: requested work items (0 = as many as stay resident)
   int work_cap = 0;        // decode: most work items the workspace is sized for
   int bt_entries = 0;      // decode: block-table entries staged per window
-  int n_qtiles = 0;        // prefill: query tiles per (sequence, head)
+  int n_qtiles = 0;        // prefill: 128-row tiles of the group * query_len rows of a (sequence, kv head)
   int kv_splits = 1;       // prefill: parts of each work item's key range (1: no split)
   int ps_log2 = -1;        // log2(page_size) or -1 if not a power of two
   bool aligned = false;    // every tile lies inside one page

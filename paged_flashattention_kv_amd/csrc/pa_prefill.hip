@@ -11,8 +11,13 @@
 // visible to the query tile is never loaded (whole-tile causal skip).
 //
 // Schedule:
-//   work item = (128-row query tile, query head, sequence), 4 waves; wave w
-//   owns query rows [32w, 32w+32) of the tile. K/V tiles are 64 keys.
+//   work item = (128-row tile, kv head, sequence), 4 waves; wave w owns rows
+//   [32w, 32w+32) of the tile. The rows are (position, query head) pairs of
+//   the G query heads that read the kv head, position-major (row r:
+//   position r / G of head kvh * G + r % G), so each K/V tile serves the
+//   whole group and a short query still fills the waves. K/V tiles are 64
+//   keys. A launch with few work items splits each key range into up to four
+//   parts run by separate workgroups, merged by the one that arrives last.
 //   Matrix core: v_mfma_f32_32x32x16_bf16 (fp32 accumulate). Scores are
 //   computed transposed, S^T = K Q^T (A = K rows from LDS, B = the wave's
 //   Q^T held in registers for the whole loop), so lane l holds 16 scores of
@@ -43,9 +48,9 @@
 // masked to -inf separately. Two LDS buffers: tile t+1 streams in while tile
 // t is computed, one barrier per tile.
 //
-// Work items are ordered so that the heaviest causal query tiles start
-// first and the query heads that share one K/V head run back to back on
-// the same XCD (shared L2).
+// Work items are ordered so that the heaviest causal row tiles start first;
+// the row tiles of one (sequence, kv head) are batch * num_kv_heads apart,
+// on one XCD (shared L2) when that is a multiple of 8.
 
 #include "pa_device.h"
 #include "pa_kernels.h"
@@ -292,25 +297,23 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   const int half = lane >> 5;  // which 8-wide k slice of an MFMA operand this lane feeds
   const int col = lane & 31;   // query row (within the wave) owned by this lane
 
-  // ---- work item: heavy query tiles first, GQA siblings together on one XCD ----
-  // Workgroup w runs part w / num_work of work item w % num_work.
+  // ---- work item: (row tile, kv head, sequence), heavy row tiles first ----
+  // The rows of a work item are (position, query head) pairs of the G query
+  // heads that read its kv head, position-major: packed row r is position
+  // r / G of head kvh * G + r % G, so every K/V tile serves the whole group
+  // and short queries still fill the waves. Workgroup w runs part
+  // w / num_work of work item w % num_work; consecutive work items of one
+  // (sequence, kv head) are batch * num_kv_heads apart, on one XCD when that
+  // is a multiple of 8.
   const int n = a.num_work;
   const int item = (int)(blockIdx.x % (unsigned)n);
   const int part = (int)(blockIdx.x / (unsigned)n);
-  int logical = item;
   const int G = a.group;
-  if (n % (8 * G) == 0) {
-    const int xcd = item & 7;  // the XCD of workgroup w is w % 8, and n is a multiple of 8
-    const int k = item >> 3;
-    logical = ((k / G) * 8 + xcd) * G + (k % G);
-  }
-  const int g = logical % G;
-  int task = logical / G;
+  int task = item;
   const int kvh = task % a.num_kv_heads;
   task /= a.num_kv_heads;
   const int b = task % a.batch;
-  const int qtile = a.n_qtiles - 1 - task / a.batch;
-  const int head = kvh * G + g;
+  const int rtile = a.n_qtiles - 1 - task / a.batch;
 
   int L = a.query_len, start = 0;
   if (a.qstart) {
@@ -320,21 +323,29 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
     L = (int)len;
     start = s0;
   }
-  const int q0 = qtile * kBM;
-  if (q0 >= L) return;  // a query tile past this sequence's rows (uniform across the work item)
+  const int R = G * L;  // packed rows of this sequence and kv head
+  const int q0 = rtile * kBM;
+  if (q0 >= R) return;  // a row tile past this sequence's rows (uniform across the work item)
   const int ctx = a.context_lens[b];
-  const int offset = ctx - L;  // query row l sits at logical position l + offset
-  const int tile_last_row = min(q0 + kBM, L) - 1;
-  const int kv_end = a.causal ? min(ctx, tile_last_row + offset + 1) : ctx;
+  const int offset = ctx - L;  // query position l sits at logical position l + offset
+  const int tile_last_pos = (min(q0 + kBM, R) - 1) / G;
+  const int kv_end = a.causal ? min(ctx, tile_last_pos + offset + 1) : ctx;
   const int n_tiles_all = (kv_end + kBN - 1) / kBN;
   // this workgroup's tiles [t_lo, n_tiles)
-  const int t_lo = (int)((int64_t)part * n_tiles_all / a.kv_splits);
-  const int n_tiles = (int)((int64_t)(part + 1) * n_tiles_all / a.kv_splits);
+  const int n_parts = a.kv_splits;
+  const int t_lo = (int)((int64_t)part * n_tiles_all / n_parts);
+  const int n_tiles = (int)((int64_t)(part + 1) * n_tiles_all / n_parts);
 
-  const int r0 = q0 + 32 * wave;  // first query row of this wave
-  const bool wave_has_rows = r0 < L;
-  const int wave_last_row = min(r0 + 31, L - 1);
-  const int wave_kv_end = a.causal ? min(ctx, wave_last_row + offset + 1) : ctx;
+  const int r0 = q0 + 32 * wave;  // first packed row of this wave
+  const bool wave_has_rows = r0 < R;
+  const int wave_first_pos = r0 / G;
+  const int wave_last_pos = (min(r0 + 31, R - 1)) / G;
+  const int wave_kv_end = a.causal ? min(ctx, wave_last_pos + offset + 1) : ctx;
+  // this lane's packed row: position pos of query head head (rows past R re-read row R - 1, never stored)
+  const int row_abs = r0 + col;
+  const int row_c = row_abs < R ? row_abs : R - 1;
+  const int pos = row_c / G;
+  const int head = kvh * G + row_c % G;
 
   const size_t head_stride = (size_t)a.page_size * D;
   const size_t page_stride = head_stride * a.num_kv_heads;
@@ -352,14 +363,12 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   // ---- Q^T operand: lane holds row r0 + col, dims 16ks + 8half .. +8 ----
   bf16x8_t qv[T::kKs];
   {
-    const int row = r0 + col;
-    const int rr = row < L ? row : 0;
-    const size_t qrow = a.qstart ? (size_t)(start + rr) * a.num_q_heads + head : ((size_t)b * a.num_q_heads + head) * L + rr;
+    const size_t qrow = a.qstart ? (size_t)(start + pos) * a.num_q_heads + head : ((size_t)b * a.num_q_heads + head) * L + pos;
     const uint16_t* qp = a.query + qrow * D + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < T::kKs; ++ks) {
       u32x4_t w = u32x4_t{0u, 0u, 0u, 0u};
-      if (row < L) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
+      if (row_abs < R) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
       qv[ks] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
@@ -388,11 +397,9 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   const uint32_t v_lane0 = (uint32_t)tile_off<D>(vk_lane, vc_lane) + vb_lane;
   const uint32_t v_lane1 = (uint32_t)tile_off<D>(vk_lane + 8, vc_lane) + vb_lane;
 
-  const int row_abs = r0 + col;
-  // this lane's mask row (MASKED only; rows past L read row L - 1, never stored)
+  // this lane's mask row (MASKED only)
   const float* mrow = a.mask;
-  if (MASKED)
-    mrow = a.mask + (size_t)b * a.msb + (size_t)head * a.msh + (size_t)(row_abs < L ? row_abs : L - 1) * a.msl;
+  if (MASKED) mrow = a.mask + (size_t)b * a.msb + (size_t)head * a.msh + (size_t)pos * a.msl;
   // One tile: wait for its loads, barrier, start the next tile's loads into
   // the other buffer, compute. The buffers are distinct LDS objects chosen
   // statically (the loop is unrolled by two), so no wait is needed between
@@ -500,14 +507,14 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
           }
         cs = 1.f;
       }
-      const bool need_mask = (t0 + kBN > ctx) || (a.causal && t0 + kBN - 1 > r0 + offset);
+      const bool need_mask = (t0 + kBN > ctx) || (a.causal && t0 + kBN - 1 > wave_first_pos + offset);
       if (need_mask) {
   #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
   #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = t0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
-            const bool vis = key < ctx && (!a.causal || key <= row_abs + offset);
+            const bool vis = key < ctx && (!a.causal || key <= pos + offset);
             acc_s[kb][i] = vis ? acc_s[kb][i] : -INFINITY;
           }
         }
@@ -573,13 +580,13 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   wait_all_loads();  // no load may still be writing this work item's LDS at exit
 
   // ---- finalize: divide by the row sum, store bf16 ----
-  if (a.kv_splits == 1) {
+  if (n_parts == 1) {
     if (!wave_has_rows) return;
     const float l_tot = sum_xor32(l_run);
-    if (row_abs >= L) return;
+    if (row_abs >= R) return;
     const float inv = 1.f / l_tot;
-    const size_t orow = a.qstart ? (size_t)(start + row_abs) * a.num_q_heads + head
-                                 : ((size_t)b * a.num_q_heads + head) * L + row_abs;
+    const size_t orow = a.qstart ? (size_t)(start + pos) * a.num_q_heads + head
+                                 : ((size_t)b * a.num_q_heads + head) * L + pos;
     uint16_t* op = a.out + orow * D;
 #pragma unroll
     for (int db = 0; db < T::kDb; ++db) {
@@ -601,7 +608,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   const size_t slot = (size_t)item * a.kv_splits + part;
   if (wave_has_rows) {
     const float l_tot = sum_xor32(l_run);
-    if (row_abs < L) {
+    if (row_abs < R) {
       const size_t r = slot * kBM + 32 * wave + col;
       if (half == 0) store_coherent_x2(a.ws_ml + r * 2, f32x2_t{m_run, l_tot});
 #pragma unroll
@@ -615,7 +622,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   wait_stores();
   __shared__ bool lds_last;
   __syncthreads();
-  if (tid == 0) lds_last = arrive_last(a.ws_ctr + item, a.epoch, (uint32_t)a.kv_splits);
+  if (tid == 0) lds_last = arrive_last(a.ws_ctr + item, a.epoch, (uint32_t)n_parts);
   __syncthreads();
   if (!lds_last) return;
   // Merge the parts in order ("Week 2 Day 5", Task 2: common maximum, one
@@ -626,11 +633,11 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   constexpr int kThrPerRow = D / 4;
   constexpr int kRowsPerPass = kThreads / kThrPerRow;
   constexpr int kMergePasses = 2;
-  const int rows_here = min(kBM, L - q0);
+  const int rows_here = min(kBM, R - q0);
   const size_t slot0 = (size_t)item * a.kv_splits;
   const int d4 = 4 * (tid % kThrPerRow);
   for (int r0p = 0; r0p < rows_here; r0p += kRowsPerPass * kMergePasses) {
-    for (int s0 = 0; s0 < a.kv_splits; s0 += kPrefillMaxSplits) {  // kv_splits <= kPrefillMaxSplits: one round
+    {  // n_parts <= kv_splits <= kPrefillMaxSplits
       f32x2_t ml[kMergePasses][kPrefillMaxSplits];
       f32x4_t av[kMergePasses][kPrefillMaxSplits];
 #pragma unroll
@@ -638,7 +645,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
         const int r = min(r0p + ps * kRowsPerPass + tid / kThrPerRow, rows_here - 1);  // re-read a valid row
 #pragma unroll
         for (int s = 0; s < kPrefillMaxSplits; ++s) {
-          const size_t rr = (slot0 + min(s, a.kv_splits - 1)) * kBM + r;
+          const size_t rr = (slot0 + min(s, n_parts - 1)) * kBM + r;
           ml[ps][s] = load_coherent_x2(a.ws_ml + rr * 2);
           av[ps][s] = load_coherent_x4(a.ws_acc + rr * D + d4);
         }
@@ -651,12 +658,12 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
         float M = -INFINITY;
 #pragma unroll
         for (int s = 0; s < kPrefillMaxSplits; ++s)
-          if (s < a.kv_splits) M = fmaxf(M, ml[ps][s].x);
+          if (s < n_parts) M = fmaxf(M, ml[ps][s].x);
         float den = 0.f;
         f32x4_t num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < kPrefillMaxSplits; ++s) {
-          if (s >= a.kv_splits) continue;
+          if (s >= n_parts) continue;
           const float f = ml[ps][s].x == -INFINITY ? 0.f : fast_exp2(ml[ps][s].x - M);
           den = fmaf(f, ml[ps][s].y, den);
           num.x = fmaf(f, av[ps][s].x, num.x);
@@ -664,9 +671,10 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
           num.z = fmaf(f, av[ps][s].z, num.z);
           num.w = fmaf(f, av[ps][s].w, num.w);
         }
-        const int row = q0 + r;
+        const int pr = q0 + r;  // packed row: position pr / G of head kvh * G + pr % G
+        const int hr = kvh * G + pr % G;
         const size_t orow =
-            a.qstart ? (size_t)(start + row) * a.num_q_heads + head : ((size_t)b * a.num_q_heads + head) * L + row;
+            a.qstart ? (size_t)(start + pr / G) * a.num_q_heads + hr : ((size_t)b * a.num_q_heads + hr) * L + pr / G;
         const u32x2_t w = {pack_bf16x2(num.x / den, num.y / den), pack_bf16x2(num.z / den, num.w / den)};
         *reinterpret_cast<u32x2_t*>(a.out + orow * D + d4) = w;
       }

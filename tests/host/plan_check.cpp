@@ -63,10 +63,10 @@ int main() {
         CHECK(p.ws_ctr_offset == 0);
         CHECK(p.bt_entries == pa::kDecodeWindow / 16 + 2);
       } else {
-        CHECK(p.n_qtiles == (L + 127) / 128);
-        // 3 * 8G work items, fewer than 512: the key range (4800 keys) splits
-        // into as many parts as keep 512 workgroups busy, at most 4
-        const int64_t nw = int64_t(3) * 8 * G * p.n_qtiles;
+        CHECK(p.n_qtiles == (G * L + 127) / 128);
+        // 3 * 8 * n_qtiles work items, fewer than 512: the key range (4800
+        // keys) splits into as many parts as keep 512 workgroups busy, at most 4
+        const int64_t nw = int64_t(3) * 8 * p.n_qtiles;
         CHECK(p.num_work == nw);
         const int want = int(std::max<int64_t>(1, std::min<int64_t>(pa::kPrefillMaxSplits, pa::kPrefillSplitTarget / nw)));
         CHECK(p.kv_splits == want);
@@ -84,11 +84,12 @@ int main() {
   CHECK(pa::make_plan(shape(1, 4, 2, 13, 128, 4, 4), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(p.schedule == pa::kSchedulePrefill && p.kv_splits == 1 && p.workspace_bytes == 0);
   CHECK(pa::make_plan(shape(1, 4, 2, 150, 128, 64, 3), 0, 0, true, &p, &err) == pa::kOk);
-  CHECK(p.num_work == 8 && p.kv_splits == 1);  // 192 keys: one part of two tiles at most
+  CHECK(p.n_qtiles == 3 && p.num_work == 6 && p.kv_splits == 1);  // 192 keys: one part of two tiles at most
   CHECK(pa::make_plan(shape(1, 4, 2, 150, 128, 64, 4), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(p.kv_splits == 2 && p.workspace_bytes > 0);
   CHECK(pa::make_plan(shape(8, 32, 8, 65, 128, 128, 29), 0, 0, true, &p, &err) == pa::kOk);
-  CHECK(p.num_work == 256 && p.kv_splits == 2);  // the chunked continuation
+  // the chunked continuation: 4 x 65 rows per kv head
+  CHECK(p.n_qtiles == 3 && p.num_work == 192 && p.kv_splits == 2);
   CHECK(pa::make_plan(shape(2, 128, 8, 256, 128, 128, 16), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(p.num_work == 512 && p.kv_splits == 1 && p.workspace_bytes == 0);
   // the five measured shapes
@@ -97,9 +98,9 @@ int main() {
   CHECK(pa::make_plan(shape(16, 32, 8, 1, 128, 16, 2048), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(p.schedule == pa::kScheduleDecode && p.aligned);
   CHECK(pa::make_plan(shape(4, 32, 8, 2048, 128, 128, 16), 0, 0, true, &p, &err) == pa::kOk);
-  CHECK(p.schedule == pa::kSchedulePrefill && p.aligned && p.n_qtiles == 16);
+  CHECK(p.schedule == pa::kSchedulePrefill && p.aligned && p.n_qtiles == 64 && p.num_work == 2048);
   CHECK(pa::make_plan(shape(8, 32, 8, 65, 128, 128, 30), 0, 0, true, &p, &err) == pa::kOk);
-  CHECK(p.schedule == pa::kSchedulePrefill && p.n_qtiles == 1);
+  CHECK(p.schedule == pa::kSchedulePrefill && p.n_qtiles == 3);
   CHECK(pa::make_plan(shape(1, 4, 2, 13, 128, 4, 4), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(p.schedule == pa::kSchedulePrefill && !p.aligned);
   // a staging window of any page size fits the block-table entries it needs
@@ -126,7 +127,7 @@ int main() {
         CHECK(dec_ws > 0);
       }
       if (v.run_prefill) {
-        CHECK(v.pre.schedule == pa::kSchedulePrefill && v.pre.n_qtiles == (maxL + 127) / 128);
+        CHECK(v.pre.schedule == pa::kSchedulePrefill && v.pre.n_qtiles == (G * maxL + 127) / 128);
         if (v.pre.kv_splits > 1) {
           CHECK(v.pre_ws_offset >= dec_ws && v.pre_ws_offset % 256 == 0);
           CHECK(v.workspace_bytes == v.pre_ws_offset + v.pre.workspace_bytes);

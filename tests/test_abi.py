@@ -189,7 +189,10 @@ def test_varlen_workspace(lib):
     assert native.varlen_workspace_bytes(64, 32, 8, 2, 128, 128, 9) == native.workspace_bytes(64, 32, 8, 2, 128, 128, 9)
     assert native.varlen_workspace_bytes(64, 32, 8, 1, 128, 128, 9) == native.workspace_bytes(64, 32, 8, 1, 128, 128, 9)
     assert native.varlen_workspace_bytes(64, 32, 8, 128, 128, 128, 9, decode_max_len=0) == 0
-    assert native.varlen_workspace_bytes(4, 64, 4, 128, 128, 128, 9) == 0  # group 16: no decode part
+    # group 16: no decode part; 256 prefill work items (16 heads x 128 positions = 2048 rows
+    # per kv head) take the key-range split, whose workspace is the uniform prefill's
+    assert native.varlen_workspace_bytes(4, 64, 4, 128, 128, 128, 9) == native.workspace_bytes(
+        4, 64, 4, 128, 128, 128, 9, native.SCHEDULE_PREFILL, 0) > 0
     with pytest.raises(native.PagedAttentionError):
         native.varlen_workspace_bytes(64, 32, 8, 128, 128, 128, 9, decode_max_len=3)
 
