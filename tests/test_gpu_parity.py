@@ -374,3 +374,68 @@ def test_decode_workspace_reuse_and_stale_counters():
         else:
             # shared segments reset their counter; the others keep the stale tag, which is ignored
             assert ((ctr == 0) | (ctr == -(1 << 32) + 5)).all()
+
+
+def _prefill_call(p, d, ws):
+    import torch
+    from paged_flashattention_kv_amd import native
+
+    out = native.paged_attention(d["query"], d["key_pages"], d["value_pages"], d["block_table"],
+                                 d["context_lens"], p.page_size, p.scale, p.causal, workspace=ws,
+                                 schedule=PREFILL)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("L,ctx,ps,Hq,Hkv,causal", [
+    (65, (1065, 3665, 2000), 128, 32, 8, True),   # chunked-continuation rows, ragged key ranges
+    (150, (150, 700), 16, 4, 2, True),             # page-crossing tiles, a part with the diagonal
+    (40, (40, 300, 5000), 64, 8, 1, False),        # group 8, non-causal, one long range
+    (3, (3, 900), 32, 6, 2, True),                 # group 3: packed rows 3 positions x 3 heads
+])
+def test_prefill_key_range_split(L, ctx, ps, Hq, Hkv, causal):
+    """Few work items: the key range splits over workgroups and merges through
+    the workspace. Against the oracle, against the unsplit run (a workspace
+    too small for the split), bit-identical across repeated calls."""
+    import torch
+    from paged_flashattention_kv_amd import native
+
+    p = small(900 + L + ps, B=len(ctx), Hq=Hq, Hkv=Hkv, L=L, ctx=ctx, ps=ps, causal=causal, poison=True)
+    max_pages = p.block_table.shape[1]
+    need = native.workspace_bytes(p.batch, Hq, Hkv, L, 128, ps, max_pages, PREFILL, 0)
+    assert need > 0, "the case must take the split"
+    say(f"key-range split L={L} ctx={ctx} ps={ps} H={Hq}/{Hkv} causal={causal} workspace={need}")
+    want = ref(p)
+    d = to_device(p)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    split = _prefill_call(p, d, ws)
+    parity(split, want, "split")
+    again = _prefill_call(p, d, ws)
+    assert np.array_equal(split, again), "the split run must be bit-reproducible"
+    unsplit = _prefill_call(p, d, torch.zeros(1, dtype=torch.uint8, device="cuda:0"))
+    parity(unsplit, want, "unsplit (no workspace)")
+    n_items = len(ctx) * Hkv * ((Hq // Hkv * L + 127) // 128)  # batch x kv heads x packed row tiles
+    ctr = ws[: 8 * n_items].view(torch.int64)
+    assert (ctr == 0).all(), "the last part resets its counter"
+
+
+def test_prefill_split_stale_counters():
+    """A workspace left by an interrupted call (counters tagged with another
+    call, arbitrary partials) is safe to reuse."""
+    import torch
+    from paged_flashattention_kv_amd import native
+
+    p = small(977, B=3, Hq=8, Hkv=2, L=70, ctx=(70, 1500, 2600), ps=64, poison=True)
+    max_pages = p.block_table.shape[1]
+    need = native.workspace_bytes(p.batch, 8, 2, 70, 128, 64, max_pages, PREFILL, 0)
+    assert need > 0
+    want = ref(p)
+    d = to_device(p)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    n_items = 3 * 2 * ((4 * 70 + 127) // 128)  # batch x kv heads x packed row tiles
+    for call in range(3):
+        if call == 1:
+            ws.view(torch.int8).random_(-128, 127)  # arbitrary partials and counter words ...
+            ws[: 8 * n_items].view(torch.int64).fill_(-(1 << 32) + 1)  # ... counters: another tag, count 1
+        got = _prefill_call(p, d, ws)
+        parity(got, want, f"stale workspace call {call}")
