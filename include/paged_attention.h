@@ -79,13 +79,16 @@ enum {
  *   causal       0 or 1
  *   workspace    device scratch of at least
  *                paged_attention_workspace_bytes(...) bytes (may be NULL when
- *                that is 0: the prefill schedule needs none). Zero-fill a
- *                workspace once before its first use: its head holds the
- *                decode schedule's arrival counters, which every successful
- *                call leaves at zero (a counter left by an interrupted call
- *                carries that call's tag and is ignored). The rest is
- *                scratch. Calls that share a workspace must be ordered on
- *                one stream.
+ *                that is 0). The decode schedule needs it; the prefill
+ *                schedule needs it only to split the key ranges of a launch
+ *                with fewer than 512 work items over several workgroups
+ *                (without it, or when it is smaller, such a prefill runs
+ *                unsplit -- a valid, slower result, not an error). Zero-fill
+ *                a workspace once before its first use: its head holds
+ *                arrival counters, which every successful call leaves at
+ *                zero (a counter left by an interrupted call carries that
+ *                call's tag and is ignored). The rest is scratch. Calls that
+ *                share a workspace must be ordered on one stream.
  *
  * Device-data preconditions (not checked; see
  * paged_attention_check_metadata): for every b,
@@ -254,7 +257,10 @@ int paged_kv_append(const void* key_new, const void* value_new, void* key_pages,
  *                paged_attention; query row l of sequence b sits at logical
  *                position context_lens[b] - L_b + l.
  *   workspace    at least paged_attention_varlen_workspace_bytes(...) bytes,
- *                zero-filled once before first use (as for paged_attention).
+ *                zero-filled once before first use (as for paged_attention:
+ *                the decode part's counters and partials, then those of the
+ *                prefill part's key-range split; a smaller workspace that
+ *                still covers the decode part runs the prefill part unsplit).
  *
  * total_query == 0 is a valid empty call: nothing is enqueued, and query /
  * out may then be NULL.
