@@ -63,8 +63,12 @@ __global__ void __launch_bounds__(kThreads) pa_kv_append(AppendArgs a) {
   const size_t dst = (((size_t)page * a.num_kv_heads + h) * a.page_size + slot) * D + chunk * 8;
   const u32x4_t k = *reinterpret_cast<const u32x4_t*>(a.key_new + src);
   const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.value_new + src);
-  *reinterpret_cast<u32x4_t*>(a.key_pages + dst) = k;
-  *reinterpret_cast<u32x4_t*>(a.value_pages + dst) = v;
+  // The page rows are written once here and read by a later attention
+  // launch, not by this one: non-temporal stores (the streaming hint) let them
+  // drain to HBM without holding cache lines (measured 14.2 -> 11.8 us for
+  // 64 MiB of K/V; the same hint on the loads gave nothing).
+  __builtin_nontemporal_store(k, reinterpret_cast<u32x4_t*>(a.key_pages + dst));
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(a.value_pages + dst));
 }
 
 template <int D>
