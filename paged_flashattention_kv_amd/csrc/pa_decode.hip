@@ -586,6 +586,11 @@ __device__ void merge_segment(const DecodeArgs& a, int32_t* lds_parts, int b, in
 
 template <int ROWS, bool ALIGNED, int D, bool MASKED>
 __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
+  // With two resident workgroups per CU the second half of the grid is the
+  // second workgroup on each CU, whose waves the memory pipeline serves after
+  // the first's; a higher issue priority for them narrows that gap (measured
+  // 1% on a whole launch). Priority changes only the order of issue.
+  if (blockIdx.x >= gridDim.x / 2) __builtin_amdgcn_s_setprio(1);
   extern __shared__ int32_t lds_bt[];
   __shared__ float lds_m[kWaves][ROWS];
   __shared__ float lds_l[kWaves][ROWS];
