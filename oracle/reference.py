@@ -3,9 +3,10 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring): the GPU path never
 imports this module.
 
-The method is exact scaled-dot-product attention in which only the order of
-loads and reductions changes ("Week 3 Day 5: Paged FlashAttention", section
-"Why Optimize the Paged Path"). So the oracle is that definition written out:
+The method approximates nothing: it reaches plain scaled-dot-product
+attention by another route through memory, and differs from it by rounding
+alone ("Week 3 Day 5: Paged FlashAttention", section "Why Optimize the Paged
+Path"). So the oracle is that definition written out:
 
 1. translate every logical key position through the block table and gather
    the sequence's history into a dense ``[H_kv, ctx, D]`` buffer -- the
