@@ -18,9 +18,11 @@
  *     s <= l + context_lens[b] - query_len (Task 2 of "Week 3 Day 5"), so the
  *     query_len rows are the last query_len positions of the context; with
  *     causal == 0 every s < context_lens[b] is visible.
- * The result is exact attention; only the order of loads and reductions
- * differs from a dense softmax. Arithmetic: bf16 loads, fp32 dot products,
- * softmax state and accumulation, bf16 (round to nearest even) output.
+ * Nothing is approximated: the kernels compute the same softmax as a dense
+ * implementation would, tile by tile, so results differ from it by rounding
+ * alone ("Week 3 Day 5", section "Why Optimize the Paged Path"). Arithmetic:
+ * bf16 loads, fp32 dot products, softmax state and accumulation, bf16 (round
+ * to nearest even) output.
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays.
@@ -75,7 +77,9 @@ enum {
  *                page holding logical positions [j*page_size, (j+1)*page_size)
  *   context_lens int32 [batch]; number of logical K/V positions of sequence b
  *   out          bf16 [batch, num_q_heads, query_len, head_dim], written once
- *   scale        multiplier of q.k (typically 1/sqrt(head_dim))
+ *   scale        multiplier of q.k (typically 1/sqrt(head_dim)); any finite
+ *                value: a negative scale is applied by negating q (exact in
+ *                bf16), and 0 weights every visible key alike
  *   causal       0 or 1
  *   workspace    device scratch of at least
  *                paged_attention_workspace_bytes(...) bytes (may be NULL when

@@ -102,7 +102,8 @@ struct DecodeArgs {
   int batch, num_q_heads, num_kv_heads, query_len, group, rows;
   int page_size, ps_log2, max_pages;
   int work_items;
-  float c;  // scale * log2(e)
+  float c;         // |scale| * log2(e), > 0 (fold_scale)
+  uint32_t qsign;  // XORed into every packed query pair: a negative scale negates q
   int causal;
   // Explicit additive mask (natural-log units) of row (b, h, l), key s at
   // mask[b*msb + h*msh + l*msl + s] for s < mask_len; keys at or past
@@ -358,8 +359,8 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
       const uint16_t* qp = a.query + row_idx(a, b, start, L, h, l) * D;
       const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(qp + dc * 8);
       const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(qp + D / 2 + dc * 8);
-      q[r][0] = lo.x; q[r][1] = lo.y; q[r][2] = lo.z; q[r][3] = lo.w;
-      q[r][4] = hi.x; q[r][5] = hi.y; q[r][6] = hi.z; q[r][7] = hi.w;
+      q[r][0] = lo.x ^ a.qsign; q[r][1] = lo.y ^ a.qsign; q[r][2] = lo.z ^ a.qsign; q[r][3] = lo.w ^ a.qsign;
+      q[r][4] = hi.x ^ a.qsign; q[r][5] = hi.y ^ a.qsign; q[r][6] = hi.z ^ a.qsign; q[r][7] = hi.w ^ a.qsign;
       last[r] = a.causal ? l + ctx - L : ctx - 1;
     } else {
 #pragma unroll
@@ -748,7 +749,9 @@ hipError_t launch_decode(const KernelArgs& k, const Plan& p, hipStream_t stream)
   a.page_size = k.page_size;
   a.ps_log2 = p.ps_log2;
   a.max_pages = k.max_pages;
-  a.c = k.scale * kLog2e;
+  const ScaleFold sf = fold_scale(k.scale);
+  a.c = sf.c;
+  a.qsign = sf.qsign;
   a.causal = k.causal;
   a.epoch = k.epoch;
   a.qstart = k.query_start;

@@ -5,6 +5,7 @@
 // under AddressSanitizer/UBSan.
 #pragma once
 
+#include <cmath>
 #include <cstddef>
 #include <cstdint>
 #include <string>
@@ -80,6 +81,30 @@ struct VarlenPlan {
   size_t pre_ws_offset = 0;  // the prefill part's workspace (key-range split) follows the decode part's
   size_t workspace_bytes = 0;
 };
+
+// How a finite `scale` reaches the kernels. Both schedules take the running
+// maximum on raw q.k scores and multiply by c = scale * log2(e) afterwards,
+// which is the maximum of the scaled scores only for c > 0. A negative scale
+// is therefore folded into the query: q.k * scale = (-q).k * |scale|, and
+// negating a bf16 value flips its sign bit exactly (qsign is XORed into every
+// packed pair of query values). A zero scale -- every visible key weighted
+// alike -- becomes the least normal float: for raw scores below 2^100 in
+// magnitude the exponent argument stays under 2^-25, so each weight rounds to
+// exactly 1 in bf16, which is the uniform softmax a zero scale defines, while
+// hidden keys (-inf scores) keep weight 0.
+struct ScaleFold {
+  float c;         // |scale| * log2(e) (> 0)
+  uint32_t qsign;  // 0x80008000 for a negative scale, else 0
+};
+
+inline ScaleFold fold_scale(float scale) {
+  constexpr float kLog2eHost = 1.4426950408889634f;
+  const float mag = std::fabs(scale);
+  ScaleFold f;
+  f.c = (mag > 0.f ? mag : 0x1p-126f) * kLog2eHost;
+  f.qsign = std::signbit(scale) && mag > 0.f ? 0x80008000u : 0u;
+  return f;
+}
 
 // Validates `s` and fills `plan`. `schedule` is 0 (auto), 1 (decode) or
 // 2 (prefill); `decode_work_items` is 0 (auto) or an explicit number of

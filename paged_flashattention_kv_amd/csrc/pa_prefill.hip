@@ -100,7 +100,8 @@ struct PrefillArgs {
   int total_query, skip_len;
   int batch, num_q_heads, num_kv_heads, query_len, group, n_qtiles;
   int page_size, ps_log2, max_pages;
-  float c;  // scale * log2(e)
+  float c;         // |scale| * log2(e), > 0 (fold_scale)
+  uint32_t qsign;  // XORed into every packed query pair: a negative scale negates q
   int causal;
   // Explicit additive mask (natural-log units, uniform layout): row (b, h, l),
   // key s at mask[b*msb + h*msh + l*msl + s] for s < mask_len; keys at or past
@@ -368,7 +369,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
 #pragma unroll
     for (int ks = 0; ks < T::kKs; ++ks) {
       u32x4_t w = u32x4_t{0u, 0u, 0u, 0u};
-      if (row_abs < R) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
+      if (row_abs < R) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks) ^ a.qsign;
       qv[ks] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
@@ -716,7 +717,9 @@ hipError_t launch_prefill(const KernelArgs& k, const Plan& p, hipStream_t stream
   a.page_size = k.page_size;
   a.ps_log2 = p.ps_log2;
   a.max_pages = k.max_pages;
-  a.c = k.scale * kLog2e;
+  const ScaleFold sf = fold_scale(k.scale);
+  a.c = sf.c;
+  a.qsign = sf.qsign;
   a.causal = k.causal;
   a.qstart = k.query_start;
   a.total_query = k.total_query;

@@ -132,6 +132,27 @@ def _stream_ptr(stream: Optional[torch.cuda.Stream], device: torch.device) -> in
     return int(s.cuda_stream)
 
 
+def _launch_stream(stream: Optional[torch.cuda.Stream], device: torch.device) -> torch.cuda.Stream:
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def _temporaries(s: torch.cuda.Stream, out: Optional[torch.Tensor], like: torch.Tensor, ws_need: int,
+                 workspace: Optional[torch.Tensor]):
+    """``out`` and the workspace, allocated (and the workspace zero-filled) on the launch stream ``s``.
+
+    Allocating on ``s`` orders the zero fill before the kernel that reads the
+    counters, and ties the memory to ``s`` in torch's caching allocator: a
+    local workspace freed on return is handed out again only to later work on
+    ``s``, after the kernel, whichever stream the caller is on.
+    """
+    with torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty_like(like)
+        if ws_need > 0 and workspace is None:
+            workspace = torch.zeros(ws_need, dtype=torch.uint8, device=like.device)
+    return out, workspace
+
+
 def _require(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, device: torch.device) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -170,7 +191,9 @@ def paged_attention(
     ``workspace`` (uint8, at least ``workspace_bytes(...)``) must be
     zero-filled before its first use and can then be reused across calls on
     one stream. The call is asynchronous on ``stream`` (default: the current
-    stream).
+    stream). Inputs must be ready on ``stream``; an ``out`` or workspace
+    allocated here is allocated on ``stream``, so work on another stream that
+    reads the returned ``out`` must first wait for ``stream``.
     """
     dev = query.device
     if dev.type != "cuda":
@@ -191,17 +214,15 @@ def paged_attention(
     max_pages = block_table.shape[1]
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
-    if out is None:
-        out = torch.empty_like(query)
-    else:
+    if out is not None:
         _require(out, "out", torch.bfloat16, 4, dev)
         if tuple(out.shape) != tuple(query.shape):
             raise ValueError("out must have the query's shape")
     need = workspace_bytes(B, Hq, Hkv, L, D, ps, max_pages, schedule, decode_work_items)
+    s = _launch_stream(stream, dev)
+    out, workspace = _temporaries(s, out, query, need, workspace)
     ws_ptr, ws_len = None, 0
     if need > 0:
-        if workspace is None:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
         if workspace.device != dev or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on the query's device")
         ws_ptr, ws_len = workspace.data_ptr(), workspace.numel() * workspace.element_size()
@@ -209,7 +230,7 @@ def paged_attention(
     rc = lib.paged_attention_ex(
         query.data_ptr(), key_pages.data_ptr(), value_pages.data_ptr(), block_table.data_ptr(),
         context_lens.data_ptr(), out.data_ptr(), B, Hq, Hkv, L, D, P, ps, max_pages, float(scale),
-        1 if causal else 0, ws_ptr, ws_len, int(schedule), int(decode_work_items), _stream_ptr(stream, dev),
+        1 if causal else 0, ws_ptr, ws_len, int(schedule), int(decode_work_items), int(s.cuda_stream),
     )
     _check(rc)
     return out
@@ -333,19 +354,17 @@ def paged_attention_varlen(
     max_pages = block_table.shape[1]
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
-    if out is None:
-        out = torch.empty_like(query)
-    else:
+    if out is not None:
         _require(out, "out", torch.bfloat16, 3, dev)
         if tuple(out.shape) != tuple(query.shape):
             raise ValueError("out must have the query's shape")
+    s = _launch_stream(stream, dev)
     if T == 0:
-        return out
+        return _temporaries(s, out, query, 0, None)[0]
     need = varlen_workspace_bytes(B, Hq, Hkv, max_query_len, D, ps, max_pages, decode_max_len, decode_work_items)
+    out, workspace = _temporaries(s, out, query, need, workspace)
     ws_ptr, ws_len = None, 0
     if need > 0:
-        if workspace is None:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
         if workspace.device != dev or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on the query's device")
         ws_ptr, ws_len = workspace.data_ptr(), workspace.numel() * workspace.element_size()
@@ -353,7 +372,7 @@ def paged_attention_varlen(
         query.data_ptr(), key_pages.data_ptr(), value_pages.data_ptr(), block_table.data_ptr(),
         context_lens.data_ptr(), query_start.data_ptr(), out.data_ptr(), B, Hq, Hkv, T, int(max_query_len), D, P,
         ps, max_pages, float(scale), 1 if causal else 0, ws_ptr, ws_len, int(decode_max_len),
-        int(decode_work_items), _stream_ptr(stream, dev),
+        int(decode_work_items), int(s.cuda_stream),
     )
     _check(rc)
     return out
@@ -429,17 +448,15 @@ def paged_attention_masked(
     max_pages = block_table.shape[1]
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
-    if out is None:
-        out = torch.empty_like(query)
-    else:
+    if out is not None:
         _require(out, "out", torch.bfloat16, 4, dev)
         if tuple(out.shape) != tuple(query.shape):
             raise ValueError("out must have the query's shape")
     need = workspace_bytes(B, Hq, Hkv, L, D, ps, max_pages, schedule, decode_work_items)
+    s = _launch_stream(stream, dev)
+    out, workspace = _temporaries(s, out, query, need, workspace)
     ws_ptr, ws_len = None, 0
     if need > 0:
-        if workspace is None:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
         if workspace.device != dev or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous tensor on the query's device")
         ws_ptr, ws_len = workspace.data_ptr(), workspace.numel() * workspace.element_size()
@@ -447,7 +464,7 @@ def paged_attention_masked(
         query.data_ptr(), key_pages.data_ptr(), value_pages.data_ptr(), block_table.data_ptr(),
         context_lens.data_ptr(), mask.data_ptr(), strides[0], strides[1], strides[2], int(mask.shape[3]),
         out.data_ptr(), B, Hq, Hkv, L, D, P, ps, max_pages, float(scale), 1 if causal else 0, ws_ptr, ws_len,
-        int(schedule), int(decode_work_items), _stream_ptr(stream, dev),
+        int(schedule), int(decode_work_items), int(s.cuda_stream),
     )
     _check(rc)
     return out

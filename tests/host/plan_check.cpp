@@ -152,6 +152,17 @@ int main() {
   // explicit decode work items reach the decode part
   CHECK(pa::make_plan_varlen(shape(4, 32, 8, 1, 128, 16, 9), -1, 5, true, &v, &err) == pa::kOk);
   CHECK(v.run_decode && !v.run_prefill && v.dec.work_items == 5 && v.dec.work_cap == 5);
+  // scale folding: c > 0 always; a negative scale flips the query's sign bits
+  {
+    const pa::ScaleFold pos = pa::fold_scale(0.0883883f);
+    CHECK(pos.qsign == 0u && pos.c > 0.127f && pos.c < 0.128f);
+    const pa::ScaleFold neg = pa::fold_scale(-0.0883883f);
+    CHECK(neg.qsign == 0x80008000u && neg.c == pos.c);
+    const pa::ScaleFold zero = pa::fold_scale(0.0f);
+    CHECK(zero.qsign == 0u && zero.c > 0.f && zero.c < 1e-37f);
+    const pa::ScaleFold nzero = pa::fold_scale(-0.0f);
+    CHECK(nzero.qsign == 0u && nzero.c == zero.c);
+  }
   if (failures == 0) std::printf("plan_check: all passed\n");
   return failures == 0 ? 0 : 1;
 }

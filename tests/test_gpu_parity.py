@@ -97,11 +97,14 @@ def test_decode_tiny_contexts_more_items_than_work(items):
 
 def test_config_long_prefill():
     p = wl.make_config("long_prefill")
-    pairs = [(0, 0), (0, 31), (1, 5), (2, 18), (3, 27), (3, 3)]
-    say("long_prefill B=4 L=ctx=2048 ps=128 pairs", pairs)
-    want = ref(p, pairs=pairs)
+    say("long_prefill B=4 L=ctx=2048 ps=128, every (b, h) against the oracle")
+    want = ref(p)
     got = run_gpu(p)
-    parity(np.stack([got[b, h] for b, h in pairs]), want, "long_prefill")
+    parity(got, want, "long_prefill (all 128 (b, h))")
+    for b in range(4):  # no (sequence, head) may hide behind the batch-wide mean
+        for h in range(32):
+            err = np.abs(got[b, h] - want[b, h])
+            assert err.max() <= 2e-2 and err.mean() <= 2e-3, (b, h, err.max(), err.mean())
     # causal row 0 of every head sees only key 0
     for b in range(4):
         for h in range(32):
@@ -122,13 +125,15 @@ def long_decode():
 
 def test_config_long_decode(long_decode):
     p = long_decode
-    pairs = [(b, h) for b in (0, 7, 15) for h in range(32)]
-    say("long_decode B=16 ctx=32768 ps=16 (sampled rows)")
-    want = ref(p, pairs=pairs)
+    say("long_decode B=16 ctx=32768 ps=16, every (b, h) against the oracle")
+    want = ref(p)
     got = run_gpu(p)
-    parity(np.stack([got[b, h] for b, h in pairs]), want, "long_decode")
+    parity(got, want, "long_decode (all 512 (b, h))")
+    for b in range(16):
+        err = np.abs(got[b] - want[b])
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, (b, err.max(), err.mean())
     got3 = run_gpu(p, schedule=DECODE, decode_work_items=3)
-    parity(np.stack([got3[b, h] for b, h in pairs]), want, "long_decode items=3")
+    parity(got3, want, "long_decode items=3 (all 512 (b, h))")
 
 
 # ------------------------------------------------------- needle probes
