@@ -30,8 +30,9 @@
  *   - The caller owns every buffer. The library allocates nothing, keeps no
  *     pointer after returning, and has no global state besides the
  *     thread-local error message, a per-device cache of how many decode
- *     work items stay resident, and a call counter that tags each call.
- *     `out` must not alias any input.
+ *     work items stay resident, a call counter that tags each call, and the
+ *     per-device scratch array of paged_attention_static (a static device
+ *     array, not an allocation). `out` must not alias any input.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously; results are valid after the stream
  *     is synchronised.
@@ -332,6 +333,34 @@ int paged_attention_varlen_check_metadata(const int32_t* block_table, const int3
                                           const int32_t* query_start, int32_t batch, int32_t max_pages,
                                           int32_t num_pages, int32_t page_size, int32_t total_query,
                                           int32_t max_query_len, int32_t causal, void* stream);
+
+/*
+ * paged_attention_static -- paged_attention for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments and result as paged_attention, minus
+ * the workspace: the decode schedule's counters and partial states (and the
+ * split prefill's) live in a scratch array that the library holds on each
+ * GPU until the process ends (paged_attention_static_scratch_bytes() bytes,
+ * 64 MiB). The first call on a device looks the array up and zero-fills it
+ * with one small kernel on `stream`; no call allocates (no hipMalloc, no
+ * hipFree, no allocating library routine).
+ *
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents: calls that may overlap on one GPU (on different streams,
+ * or from several threads without ordering) race on it and must be ordered
+ * on one stream by the caller. Calls with a decode schedule that needs more
+ * scratch than the array holds return PA_ERR_UNSUPPORTED before any launch;
+ * a prefill whose key-range split needs more runs unsplit (a valid, slower
+ * result).
+ */
+int paged_attention_static(const void* query, const void* key_pages, const void* value_pages,
+                           const int32_t* block_table, const int32_t* context_lens, void* out, int32_t batch,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t query_len, int32_t head_dim,
+                           int32_t num_pages, int32_t page_size, int32_t max_pages, float scale, int32_t causal,
+                           void* stream);
+
+/* Bytes of the per-GPU scratch array paged_attention_static uses. */
+size_t paged_attention_static_scratch_bytes(void);
 
 /* Message describing the last error returned on the calling thread ("" if none). */
 const char* paged_attention_last_error(void);

@@ -9,6 +9,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -133,6 +134,54 @@ int run_uniform(const void* query, const void* key_pages, const void* value_page
   return PA_OK;
 }
 
+// ---- the library's own scratch for paged_attention_static ----
+//
+// One array per GPU, held until the process ends: the decode schedule's
+// arrival counters and partial states, and the split prefill's, for callers
+// that cannot allocate. 64 MiB covers every decode launch of head dim 128
+// (8 query rows per kv head, 2048 work items: 17 MB) and every split prefill
+// of head dim 128 (at most 512 parts of 128 rows: 34 MB).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Zero-fills the scratch once per device: its head holds arrival counters.
+__global__ void zero_scratch(uint4* p, size_t n16) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += size_t(gridDim.x) * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this device's scratch (the host-side name of the
+// array is only a stand-in), looked up and zero-filled on the first call on
+// that device. Returns nullptr with the error set on failure.
+void* device_scratch(hipStream_t stream, int* code) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *code = set_error(PA_ERR_LAUNCH, "no current HIP device");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *code = set_error(PA_ERR_LAUNCH, std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e));
+      return nullptr;
+    }
+    hipLaunchKernelGGL(zero_scratch, dim3(1024), dim3(256), 0, stream, static_cast<uint4*>(ptr), kScratchBytes / 16);
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+      *code = set_error(PA_ERR_LAUNCH, std::string("scratch fill failed: ") + hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -180,6 +229,35 @@ int paged_attention(const void* query, const void* key_pages, const void* value_
                             max_pages, scale, causal, workspace, workspace_bytes, PA_SCHEDULE_AUTO, 0,
                             stream);
 }
+
+int paged_attention_static(const void* query, const void* key_pages, const void* value_pages,
+                           const int32_t* block_table, const int32_t* context_lens, void* out, int32_t batch,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t query_len, int32_t head_dim,
+                           int32_t num_pages, int32_t page_size, int32_t max_pages, float scale, int32_t causal,
+                           void* stream) {
+  if (!query || !key_pages || !value_pages || !block_table || !context_lens || !out)
+    return set_error(PA_ERR_INVALID, "a tensor pointer is NULL");
+  // sizes next: nothing is touched for a call the scratch cannot serve
+  pa::Plan plan;
+  std::string err;
+  const pa::Shape s = make_shape(batch, num_q_heads, num_kv_heads, query_len, head_dim, num_pages, page_size,
+                                 max_pages, causal != 0);
+  const int rc = pa::make_plan(s, PA_SCHEDULE_AUTO, 0, true, &plan, &err);
+  if (rc != pa::kOk) return set_error(rc, err);
+  if (plan.schedule == pa::kScheduleDecode && plan.workspace_bytes > kScratchBytes)
+    return set_error(PA_ERR_UNSUPPORTED, "the decode schedule needs " + std::to_string(plan.workspace_bytes) +
+                                             " bytes of scratch; paged_attention_static holds " +
+                                             std::to_string(kScratchBytes) + " (use paged_attention)");
+  int code = PA_OK;
+  void* ws = device_scratch(static_cast<hipStream_t>(stream), &code);
+  if (ws == nullptr) return code;
+  // a split prefill that needs more than the scratch runs unsplit (as with a short workspace)
+  return paged_attention(query, key_pages, value_pages, block_table, context_lens, out, batch, num_q_heads,
+                         num_kv_heads, query_len, head_dim, num_pages, page_size, max_pages, scale, causal, ws,
+                         kScratchBytes, stream);
+}
+
+size_t paged_attention_static_scratch_bytes(void) { return kScratchBytes; }
 
 size_t paged_attention_workspace_bytes_ex(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                           int32_t query_len, int32_t head_dim, int32_t page_size,

@@ -43,6 +43,8 @@ EXPORTED = (
     "paged_attention_varlen_workspace_bytes",
     "paged_attention_varlen_check_metadata",
     "paged_attention_masked",
+    "paged_attention_static",
+    "paged_attention_static_scratch_bytes",
 )
 
 _lib = None
@@ -96,6 +98,10 @@ def load() -> ctypes.CDLL:
         lib.paged_attention_masked.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32, i32, i32, i32,
                                                i32, i32, i32, i32, f32, i32, vp, sz, i32, i32, vp]
         lib.paged_attention_masked.restype = ctypes.c_int
+        lib.paged_attention_static.argtypes = ex_args[:16] + [vp]
+        lib.paged_attention_static.restype = ctypes.c_int
+        lib.paged_attention_static_scratch_bytes.argtypes = []
+        lib.paged_attention_static_scratch_bytes.restype = sz
         lib.paged_attention_last_error.argtypes = []
         lib.paged_attention_last_error.restype = ctypes.c_char_p
         _lib = lib

@@ -31,7 +31,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 15
     assert sorted(native.EXPORTED) == names
     raw = ctypes.CDLL(native.LIB_PATH)
     for n in names:
@@ -225,3 +225,17 @@ def test_host_planning_under_sanitizers(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "all passed" in r.stdout
+
+
+def test_static_entry_point_rejects_before_any_launch(lib):
+    # argument errors of the allocation-free entry point come back before it
+    # touches a device (this host has none): NULL tensors, then a decode shape
+    # whose counters and partials would not fit the 64 MiB scratch
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("host-only error paths")
+    assert lib.paged_attention_static_scratch_bytes() == 64 << 20
+    rc = lib.paged_attention_static(None, None, None, None, None, None, 1, 32, 8, 1, 128, 10, 16, 4,
+                                    ctypes.c_float(0.088), 1, None)
+    assert rc == native.PA_ERR_INVALID
