@@ -257,12 +257,18 @@ __device__ __forceinline__ void compute_stage(const Stage& st, const float (&mv)
   // rounded weights.
   static_assert(kTK % 2 == 0, "keys are paired for the packed weights");
   uint32_t pp[ROWS][kTK / 2];
+  // the rows' step maxima first: independent reductions that overlap
+  float tmaxes[ROWS];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     float tmax = s[r][0];
 #pragma unroll
     for (int i = 1; i < kTK; ++i) tmax = fmaxf(tmax, s[r][i]);
-    tmax = max_stride<LPK>(tmax) * c;
+    tmaxes[r] = max_stride<LPK>(tmax) * c;
+  }
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const float tmax = tmaxes[r];
     if (tmax > rs.m[r] + kTau) {  // uniform across the wave
       const float alpha = fast_exp2(rs.m[r] - tmax);  // 0 when the old reference is -inf
       rs.m[r] = tmax;

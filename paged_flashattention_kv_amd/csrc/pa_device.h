@@ -53,6 +53,18 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, false));
 }
 
+// Max / sum of x over the lane pair (l, l ^ 16): v_permlane16_swap hands
+// every lane the values of both lanes of its pair (a VALU exchange, where a
+// shuffle would be an LDS round trip).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
 // Sum over the N consecutive lanes of an aligned group of N (N = 4, 8, 16
 // or 32); every lane of the group receives the total.
 template <int N>
@@ -62,7 +74,7 @@ __device__ __forceinline__ float sum_lanes(float x) {
   x += dpp<kDppQuadXor2>(x);
   if (N >= 8) x += dpp<kDppRowHalfMirror>(x);
   if (N >= 16) x += dpp<kDppRowMirror>(x);
-  if (N >= 32) x += __shfl_xor(x, 16);
+  if (N >= 32) x = sum_xor16(x);
   return x;
 }
 
@@ -85,7 +97,7 @@ __device__ __forceinline__ float max_stride(float x) {
   static_assert(S == 4 || S == 8 || S == 16 || S == 32, "strides of 4, 8, 16 or 32 lanes");
   if (S == 4) x = fmaxf(x, dpp<kDppRowRor4>(x));
   if (S <= 8) x = fmaxf(x, dpp<kDppRowRor8>(x));
-  if (S <= 16) x = fmaxf(x, __shfl_xor(x, 16));
+  if (S <= 16) x = max_xor16(x);
   return max_xor32(x);
 }
 
@@ -94,7 +106,7 @@ __device__ __forceinline__ float sum_stride(float x) {
   static_assert(S == 4 || S == 8 || S == 16 || S == 32, "strides of 4, 8, 16 or 32 lanes");
   if (S == 4) x += dpp<kDppRowRor4>(x);
   if (S <= 8) x += dpp<kDppRowRor8>(x);
-  if (S <= 16) x += __shfl_xor(x, 16);
+  if (S <= 16) x = sum_xor16(x);
   return sum_xor32(x);
 }
 

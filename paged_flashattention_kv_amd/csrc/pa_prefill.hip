@@ -124,17 +124,25 @@ struct PrefillArgs {
 __device__ __forceinline__ int div_ps(int s, int ps, int ps_log2) { return ps_log2 >= 0 ? (s >> ps_log2) : s / ps; }
 
 // 16-byte chunk c of key row `key` sits at chunk position c ^ swz(key). The
-// swizzle spreads the K fragment reads (32 keys, one chunk each) and the
-// transposed V reads over the LDS banks. 256-byte rows (D = 128) and longer
-// ones take a 4-bit swizzle of the low chunk bits; 128-byte rows (D = 64),
-// two to a bank line, a bit-reversed 3-bit index of the key pair.
+// swizzle spreads both kinds of fragment read over the 64 LDS banks (a
+// 256-byte bank line):
+//  - K (ds_read_b128): 16 lanes served together read one chunk of 16
+//    consecutive keys, so key -> swz(key) must be one-to-one on every
+//    aligned group of 16 keys;
+//  - V^T (ds_read_b64_tr_b16): 32 lanes served together read chunks
+//    4db .. 4db+3 of an aligned group of 4 keys, so the 4 keys must differ in
+//    the top two bits of the 4-bit swizzle (the low two are the chunk's).
+// 256-byte rows (D = 128) and longer ones take the low two key bits as the
+// top two swizzle bits and key bits 2-3 as the low two. 128-byte rows
+// (D = 64), two to a bank line, take a bit-reversed 3-bit index of the key
+// pair (even and odd keys sit in different halves of the line).
 template <int D>
 __device__ __forceinline__ int swz(int key) {
   if (D == 64) {
     const int j = (key >> 1) & 7;
     return ((j & 1) << 2) | (j & 2) | ((j >> 2) & 1);
   }
-  return ((key & 7) << 1) | ((key >> 3) & 1);
+  return ((key & 3) << 2) | ((key >> 2) & 3);
 }
 
 // Byte offset of (key, chunk) inside a tile buffer.
