@@ -396,10 +396,10 @@ def mixed_roofline_us(p) -> dict:
     prefill part's flops at the bf16 matrix peak (the two launches run one after the other)."""
     ql = p.query_lens
     group = p.num_q_heads // p.num_kv_heads
-    if group * p.max_query_len <= 8:
+    if group * p.max_query_len <= 4:  # the library's automatic split (decode while G * L <= 4)
         dec_max = p.max_query_len
     else:
-        dec_max = 1 if group <= 8 else 0
+        dec_max = 1 if group <= 4 else 0
     dec = (ql >= 1) & (ql <= dec_max)
     pre = ql > dec_max
     ctx = p.context_lens.astype("int64")

@@ -54,7 +54,7 @@ enum {
   PA_OK = 0,
   PA_ERR_INVALID = -1,     /* null pointer, non-positive size, H_q % H_kv != 0,
                               max_pages * page_size < query_len, ... */
-  PA_ERR_UNSUPPORTED = -2, /* head_dim not 64, 128 or 256, or a size past a kernel limit */
+  PA_ERR_UNSUPPORTED = -2, /* head_dim not a multiple of 8 in [8, 256], or a size past a kernel limit */
   PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   PA_ERR_LAUNCH = -4,      /* the HIP runtime rejected a launch */
   PA_ERR_METADATA = -5     /* paged_attention_check_metadata found bad data */
@@ -103,12 +103,14 @@ enum {
  * slots at or past context_lens[b] are never read and may hold anything.
  *
  * Dispatch (inside the library, "Week 3 Day 5", Task 4): a short query
- * (query_len * num_q_heads / num_kv_heads <= 8) runs the decode schedule,
- * anything longer the prefill schedule. Supported: head_dim 64, 128 or 256
- * ("Week 3 Day 5", Task 1, writes its matrix kernel for head dim 128 and
- * keeps generic controls for the rest; here both schedules are instantiated
- * for each of the three), page_size >= 1, any batch, GQA ratio and context
- * length that fit int32.
+ * (query_len * num_q_heads / num_kv_heads <= 4 rows per kv head) runs the
+ * decode schedule, anything longer the prefill schedule -- the crossover
+ * measured on MI355X over query lengths, contexts and GQA ratios. Supported:
+ * head_dim any multiple of 8 from 8 to 256 ("Week 3 Day 5", Task 1, writes
+ * its matrix kernel for head dim 128 and keeps generic controls for the
+ * rest; here both schedules have instances for 64, 128 and 256, and any
+ * other head dim runs the next larger instance with its extra dims masked),
+ * page_size >= 1, any batch, GQA ratio and context length that fit int32.
  */
 int paged_attention(const void* query, const void* key_pages, const void* value_pages,
                     const int32_t* block_table, const int32_t* context_lens, void* out,
@@ -231,7 +233,7 @@ int paged_attention_check_metadata(const int32_t* block_table, const int32_t* co
  * position) pairs of one call map to the same page slot.
  * The new K/V buffers must not overlap the pools, nor the two pools each
  * other. Asynchronous on `stream`; nothing is allocated. Returns PA_OK,
- * PA_ERR_INVALID, PA_ERR_UNSUPPORTED (head_dim not 64, 128 or 256) or
+ * PA_ERR_INVALID, PA_ERR_UNSUPPORTED (head_dim not a multiple of 8 in [8, 256]) or
  * PA_ERR_LAUNCH;
  * nothing is launched unless every check passes.
  */
@@ -279,9 +281,9 @@ int paged_kv_append(const void* key_new, const void* value_new, void* key_pages,
  * (its rows are not written), so broken offsets never cause a stray access.
  *
  * Dispatch, with group = num_q_heads / num_kv_heads: when group *
- * max_query_len <= 8 every sequence runs the decode schedule (the rule of
+ * max_query_len <= 4 every sequence runs the decode schedule (the rule of
  * paged_attention); otherwise one-token queries run the decode schedule
- * (none when group > 8) and every longer query the prefill schedule -- the
+ * (none when group > 4) and every longer query the prefill schedule -- the
  * decode schedule's cost grows with its widest sequence's rows. Two launches
  * on `stream`, the second only when some query is longer than the decode
  * bound.

@@ -37,9 +37,12 @@ struct AppendArgs {
   const int32_t* context_lens;
   int64_t rows;  // batch * num_kv_heads * new_len
   int num_kv_heads, new_len, num_pages, page_size, ps_log2, max_pages;
+  int dv;  // row length in elements (<= D; lanes past it copy nothing)
 };
 
-// D/8 lanes copy one row of D bf16 values (16 bytes each).
+// D/8 lanes copy one row of dv <= D bf16 values (16 bytes each; a head dim
+// that is not 64, 128 or 256 runs the next larger instance with its last
+// lanes idle).
 template <int D>
 __global__ void __launch_bounds__(kThreads) pa_kv_append(AppendArgs a) {
   constexpr int kLanesPerRow = D / 8;
@@ -47,6 +50,7 @@ __global__ void __launch_bounds__(kThreads) pa_kv_append(AppendArgs a) {
   const int64_t row = (int64_t)blockIdx.x * kRowsPerItem + threadIdx.x / kLanesPerRow;
   if (row >= a.rows) return;
   const int chunk = threadIdx.x % kLanesPerRow;
+  if (chunk * 8 >= a.dv) return;
   const int l = (int)(row % a.new_len);
   const int64_t bh = row / a.new_len;
   const int h = (int)(bh % a.num_kv_heads);
@@ -59,8 +63,8 @@ __global__ void __launch_bounds__(kThreads) pa_kv_append(AppendArgs a) {
   const int32_t page = a.block_table[(size_t)b * a.max_pages + lp];
   if (page < 0 || page >= a.num_pages) return;
   const int slot = s - lp * a.page_size;
-  const size_t src = (size_t)row * D + chunk * 8;
-  const size_t dst = (((size_t)page * a.num_kv_heads + h) * a.page_size + slot) * D + chunk * 8;
+  const size_t src = (size_t)row * a.dv + chunk * 8;
+  const size_t dst = (((size_t)page * a.num_kv_heads + h) * a.page_size + slot) * a.dv + chunk * 8;
   const u32x4_t k = *reinterpret_cast<const u32x4_t*>(a.key_new + src);
   const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.value_new + src);
   // The page rows are written once here and read by a later attention
@@ -98,7 +102,8 @@ hipError_t launch_append(const AppendKernelArgs& k, hipStream_t stream) {
   for (int e = 0; e < 31; ++e)
     if ((1 << e) == k.page_size) a.ps_log2 = e;
   a.max_pages = k.max_pages;
-  switch (k.head_dim) {
+  a.dv = k.head_dim;
+  switch (instance_dim(k.head_dim)) {
     case 64: return launch_dim<64>(a, stream);
     case 256: return launch_dim<256>(a, stream);
     default: return launch_dim<128>(a, stream);

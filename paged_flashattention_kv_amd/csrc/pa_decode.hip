@@ -34,11 +34,16 @@
 // reference is shared by the whole wave, so wave partials combine without
 // rescaling; the 4 waves merge in LDS through a common maximum. Register
 // stages rotate so the next steps' K/V loads are in flight while a step is
-// computed.
+// computed. Head dims other than 64, 128 and 256 (any multiple of 8 up to
+// 256) run the next larger instance D: rows are dv elements long in memory,
+// the query's dims past dv are zero, a lane's chunk past dv re-reads the
+// row's first chunk (finite data, weighted by a zero query) and no output
+// dim past dv is stored.
 //
 // Page translation ("Week 3 Day 5", Task 1): the block-table entries of a
-// 2048-key window are staged in LDS. Aligned path (page_size % 32 == 0): a
-// step lies inside one page, found with one table entry. Generic path: every
+// 2048-key window are staged in LDS. Aligned path (page_size a multiple of
+// the wave step, 2048 / D keys): a step lies inside one page, found with one
+// table entry. Generic path: every
 // key row is translated on its own (steps that cross page boundaries, e.g.
 // 16-token pages). Keys past the piece end are never loaded from their own
 // (possibly missing) page; their scores are forced to -inf by a separate
@@ -99,6 +104,7 @@ struct DecodeArgs {
   // 1 .. query_len. nullptr: the uniform [B, H_q, query_len, 128] layout.
   const int32_t* qstart;
   int total_query;
+  int dv;  // head dim of query, pages and out (<= D: dims past it are masked)
   int batch, num_q_heads, num_kv_heads, query_len, group, rows;
   int page_size, ps_log2, max_pages;
   int work_items;
@@ -127,6 +133,8 @@ struct Pager {
   size_t page_stride, head_off;
   int lp0, s0, s1, page_size, ps_log2;
   int kg, dc;
+  int dv;      // row length in elements
+  int c0, c1;  // element offsets of the lane's two chunks in a row (a masked chunk re-reads chunk 0)
 };
 
 // Every K/V row is read once per launch. At head dims 128 and 256 the loads
@@ -144,9 +152,11 @@ __device__ __forceinline__ u32x4_t load_kv(const uint16_t* p) {
 // [8dc, 8dc+8) and [D/2+8dc, D/2+8dc+8). Keys at or past the split end are
 // redirected to the split's first key (always a valid row) so every load is
 // unconditional; their scores are masked to -inf and their weight is 0.
-template <bool ALIGNED, int D>
+template <bool ALIGNED, int D, bool GEN>
 __device__ __forceinline__ void load_stage(const Pager& g, int t0, Stage& st) {
   constexpr int KPI = Geo<D>::KPI;
+  const int dvr = GEN ? g.dv : D;  // row length in memory
+  const int c0 = GEN ? g.c0 : g.dc * 8, c1 = GEN ? g.c1 : D / 2 + g.dc * 8;
   size_t row[kTK];
   if (ALIGNED) {
     // page_size % kStep == 0 and t0 % kStep == 0: the step lies inside one
@@ -154,11 +164,11 @@ __device__ __forceinline__ void load_stage(const Pager& g, int t0, Stage& st) {
     const int tb = t0 < g.s1 ? t0 : g.s0;
     const int lp = div_ps(tb, g.page_size, g.ps_log2);
     const size_t base = (size_t)g.lds_bt[lp - g.lp0] * g.page_stride + g.head_off +
-                        (size_t)(tb - lp * g.page_size) * D;
+                        (size_t)(tb - lp * g.page_size) * dvr;
 #pragma unroll
     for (int i = 0; i < kTK; ++i) {
       const int key = t0 + g.kg + KPI * i;
-      row[i] = key < g.s1 ? base + (size_t)(g.kg + KPI * i) * D : base;
+      row[i] = key < g.s1 ? base + (size_t)(g.kg + KPI * i) * dvr : base;
     }
   } else {
 #pragma unroll
@@ -166,18 +176,18 @@ __device__ __forceinline__ void load_stage(const Pager& g, int t0, Stage& st) {
       int key = t0 + g.kg + KPI * i;
       key = key < g.s1 ? key : g.s0;
       const int lp = div_ps(key, g.page_size, g.ps_log2);
-      row[i] = (size_t)g.lds_bt[lp - g.lp0] * g.page_stride + g.head_off + (size_t)(key - lp * g.page_size) * D;
+      row[i] = (size_t)g.lds_bt[lp - g.lp0] * g.page_stride + g.head_off + (size_t)(key - lp * g.page_size) * dvr;
     }
   }
 #pragma unroll
   for (int i = 0; i < kTK; ++i) {
-    st.k[i][0] = load_kv<D>(g.kpages + row[i] + g.dc * 8);
-    st.k[i][1] = load_kv<D>(g.kpages + row[i] + D / 2 + g.dc * 8);
+    st.k[i][0] = load_kv<D>(g.kpages + row[i] + c0);
+    st.k[i][1] = load_kv<D>(g.kpages + row[i] + c1);
   }
 #pragma unroll
   for (int i = 0; i < kTK; ++i) {
-    st.v[i][0] = load_kv<D>(g.vpages + row[i] + g.dc * 8);
-    st.v[i][1] = load_kv<D>(g.vpages + row[i] + D / 2 + g.dc * 8);
+    st.v[i][0] = load_kv<D>(g.vpages + row[i] + c0);
+    st.v[i][1] = load_kv<D>(g.vpages + row[i] + c1);
   }
 }
 
@@ -339,7 +349,7 @@ __device__ __forceinline__ int64_t gran_begin(int64_t w, int64_t total, int64_t 
 // rows of that kv head (sequence b has L rows from token `start`). Merges
 // the 4 waves' states and either stores the output (the piece is the whole
 // segment) or leaves the partial state in the workspace slot.
-template <int ROWS, bool ALIGNED, int D, bool MASKED>
+template <int ROWS, bool ALIGNED, int D, bool MASKED, bool GEN>
 __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_bt, float (*lds_m)[ROWS],
                                              float (*lds_l)[ROWS], float (*lds_acc)[ROWS][D], int b, int kvh,
                                              int ctx, int L, int start, int k0, int k1, bool direct, int slot) {
@@ -362,11 +372,15 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
       const int h = kvh * a.group + r / L;
       const int l = r % L;
       if (MASKED) mrow[r] = a.mask + (size_t)b * a.msb + (size_t)h * a.msh + (size_t)l * a.msl;
-      const uint16_t* qp = a.query + row_idx(a, b, start, L, h, l) * D;
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(qp + dc * 8);
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(qp + D / 2 + dc * 8);
-      q[r][0] = lo.x ^ a.qsign; q[r][1] = lo.y ^ a.qsign; q[r][2] = lo.z ^ a.qsign; q[r][3] = lo.w ^ a.qsign;
-      q[r][4] = hi.x ^ a.qsign; q[r][5] = hi.y ^ a.qsign; q[r][6] = hi.z ^ a.qsign; q[r][7] = hi.w ^ a.qsign;
+      // dims past dv are zero in the query, so their (re-read) keys add nothing
+      const uint16_t* qp = a.query + row_idx(a, b, start, L, h, l) * (GEN ? a.dv : D);
+      u32x4_t lo = u32x4_t{0u, 0u, 0u, 0u}, hi = lo;
+      const bool use_lo = !GEN || dc * 8 < a.dv, use_hi = !GEN || D / 2 + dc * 8 < a.dv;
+      const uint32_t sl = use_lo ? a.qsign : 0u, sh = use_hi ? a.qsign : 0u;
+      if (use_lo) lo = *reinterpret_cast<const u32x4_t*>(qp + dc * 8);
+      if (use_hi) hi = *reinterpret_cast<const u32x4_t*>(qp + D / 2 + dc * 8);
+      q[r][0] = lo.x ^ sl; q[r][1] = lo.y ^ sl; q[r][2] = lo.z ^ sl; q[r][3] = lo.w ^ sl;
+      q[r][4] = hi.x ^ sh; q[r][5] = hi.y ^ sh; q[r][6] = hi.z ^ sh; q[r][7] = hi.w ^ sh;
       last[r] = a.causal ? l + ctx - L : ctx - 1;
     } else {
 #pragma unroll
@@ -391,8 +405,11 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
   g.kpages = a.kpages;
   g.vpages = a.vpages;
   g.lds_bt = lds_bt;
-  g.page_stride = (size_t)a.page_size * D * a.num_kv_heads;
-  g.head_off = (size_t)kvh * a.page_size * D;
+  g.page_stride = (size_t)a.page_size * (GEN ? a.dv : D) * a.num_kv_heads;
+  g.head_off = (size_t)kvh * a.page_size * (GEN ? a.dv : D);
+  g.dv = a.dv;
+  g.c0 = dc * 8 < a.dv ? dc * 8 : 0;
+  g.c1 = D / 2 + dc * 8 < a.dv ? D / 2 + dc * 8 : 0;
   g.page_size = a.page_size;
   g.ps_log2 = a.ps_log2;
   g.kg = kg;
@@ -424,14 +441,14 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
       float mv[kStages][MASKED ? ROWS : 1][kTK];  // mask entries riding with each stage
 #pragma unroll
       for (int i = 0; i < kStages - 1; ++i) {
-        load_stage<ALIGNED, D>(g, t + i * kStride, st[i]);
+        load_stage<ALIGNED, D, GEN>(g, t + i * kStride, st[i]);
         if constexpr (MASKED) load_mask<ROWS, D>(mrow, a.mask_len, t + i * kStride, kg, mv[i]);
       }
       bool done = false;
       while (!done) {
 #pragma unroll
         for (int j = 0; j < kStages; ++j) {
-          load_stage<ALIGNED, D>(g, t + (kStages - 1) * kStride, st[(j + kStages - 1) % kStages]);
+          load_stage<ALIGNED, D, GEN>(g, t + (kStages - 1) * kStride, st[(j + kStages - 1) % kStages]);
           if constexpr (MASKED)
             load_mask<ROWS, D>(mrow, a.mask_len, t + (kStages - 1) * kStride, kg, mv[(j + kStages - 1) % kStages]);
           compute_stage<ROWS, D, MASKED>(st[j], mv[j], t, kb, a.mask_len, q, last, min_last, a.c, kg, rs);
@@ -491,7 +508,7 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
     if (direct) {
       const int h = kvh * a.group + r / L;
       const int l = r % L;
-      a.out[row_idx(a, b, start, L, h, l) * D + d] = to_bf16(num / den);
+      if (!GEN || d < a.dv) a.out[row_idx(a, b, start, L, h, l) * (GEN ? a.dv : D) + d] = to_bf16(num / den);
     } else {
       // device-coherent stores (no cache-wide fence needed; see arrive_last)
       store_coherent(a.ws_acc + (part + r) * D + d, num);
@@ -530,7 +547,7 @@ __device__ __forceinline__ SegmentItems segment_items(int64_t S, int64_t E, int6
 // with maximum -inf (no visible key) contribute 0.
 constexpr int kMergeBatch = 8;
 
-template <int D>
+template <int D, bool GEN>
 __device__ void merge_segment(const DecodeArgs& a, int32_t* lds_parts, int b, int kvh, int L, int start, int64_t S,
                               const SegmentItems& it, int64_t total) {
   const int64_t P = a.work_items;
@@ -583,15 +600,15 @@ __device__ void merge_segment(const DecodeArgs& a, int32_t* lds_parts, int b, in
         }
       }
     }
-    if (idx < n_rd) {
+    if (idx < n_rd && (!GEN || d < a.dv)) {
       const int h = kvh * a.group + r / L;
       const int l = r % L;
-      a.out[row_idx(a, b, start, L, h, l) * D + d] = to_bf16(num / den);
+      a.out[row_idx(a, b, start, L, h, l) * (GEN ? a.dv : D) + d] = to_bf16(num / den);
     }
   }
 }
 
-template <int ROWS, bool ALIGNED, int D, bool MASKED>
+template <int ROWS, bool ALIGNED, int D, bool MASKED, bool GEN>
 __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
   // With two resident workgroups per CU the second half of the grid is the
   // second workgroup on each CU, whose waves the memory pipeline serves after
@@ -662,7 +679,7 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
     const int k0 = (int)((G - S) * kGran);
     const int k1 = (int)min((gend - S) * kGran, (int64_t)ctx);
     const bool direct = G == S && gend == E;
-    decode_piece<ROWS, ALIGNED, D, MASKED>(a, lds_bt, lds_m, lds_l, lds_acc, b, kvh, ctx, L, start, k0, k1, direct,
+    decode_piece<ROWS, ALIGNED, D, MASKED, GEN>(a, lds_bt, lds_m, lds_l, lds_acc, b, kvh, ctx, L, start, k0, k1, direct,
                                    nth == 0 ? 0 : 1);
     if (!direct) {
       // publish this piece, then the last of the segment's work items merges it
@@ -671,7 +688,7 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
       const SegmentItems it = segment_items(S, E, total, a.work_items);
       if (tid == 0) lds_last = arrive_last(a.ws_ctr + (size_t)b * a.num_kv_heads + kvh, a.epoch, it.count);
       __syncthreads();
-      if (lds_last) merge_segment<D>(a, lds_parts, b, kvh, L, start, S, it, total);
+      if (lds_last) merge_segment<D, GEN>(a, lds_parts, b, kvh, L, start, S, it, total);
     }
     G = gend;
     ++nth;
@@ -682,16 +699,16 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
   }
 }
 
-template <int ROWS, bool ALIGNED, int D, bool MASKED>
+template <int ROWS, bool ALIGNED, int D, bool MASKED, bool GEN>
 hipError_t launch_work(const DecodeArgs& a, size_t lds_bytes, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_decode_work<ROWS, ALIGNED, D, MASKED>), dim3((unsigned)a.work_items), dim3(kThreads), lds_bytes,
+  hipLaunchKernelGGL((pa_decode_work<ROWS, ALIGNED, D, MASKED, GEN>), dim3((unsigned)a.work_items), dim3(kThreads), lds_bytes,
                      stream, a);
   return hipGetLastError();
 }
 
 // Work items the GPU keeps resident for one kernel instance (cached per
 // device; registers, not shared memory, bound it for every page size).
-template <int ROWS, bool ALIGNED, int D, bool MASKED>
+template <int ROWS, bool ALIGNED, int D, bool MASKED, bool GEN>
 int resident_items(size_t lds_bytes) {
   static int cache[64] = {0};
   int dev = 0;
@@ -699,7 +716,7 @@ int resident_items(size_t lds_bytes) {
   if (cache[dev] > 0) return cache[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)pa_decode_work<ROWS, ALIGNED, D, MASKED>, kThreads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)pa_decode_work<ROWS, ALIGNED, D, MASKED, GEN>, kThreads,
                                                    lds_bytes) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   const int n = cus * per_cu;
@@ -709,12 +726,18 @@ int resident_items(size_t lds_bytes) {
 
 template <int ROWS, int D, bool MASKED>
 hipError_t launch_rows(DecodeArgs& a, bool aligned, int requested, int cap, size_t lds, hipStream_t st) {
-  if (aligned) {
-    a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, true, D, MASKED>(lds));
-    return launch_work<ROWS, true, D, MASKED>(a, lds, st);
+  if (a.dv != D) {
+    // a head dim without an instance of its own: the next larger one, masked
+    // dims, the per-row loader
+    a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, false, D, MASKED, true>(lds));
+    return launch_work<ROWS, false, D, MASKED, true>(a, lds, st);
   }
-  a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, false, D, MASKED>(lds));
-  return launch_work<ROWS, false, D, MASKED>(a, lds, st);
+  if (aligned) {
+    a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, true, D, MASKED, false>(lds));
+    return launch_work<ROWS, true, D, MASKED, false>(a, lds, st);
+  }
+  a.work_items = requested > 0 ? requested : min(cap, resident_items<ROWS, false, D, MASKED, false>(lds));
+  return launch_work<ROWS, false, D, MASKED, false>(a, lds, st);
 }
 
 template <int D, bool MASKED>
@@ -762,6 +785,7 @@ hipError_t launch_decode(const KernelArgs& k, const Plan& p, hipStream_t stream)
   a.epoch = k.epoch;
   a.qstart = k.query_start;
   a.total_query = k.total_query;
+  a.dv = k.head_dim;
   a.mask = k.mask;
   a.msb = k.mask_stride_b;
   a.msh = k.mask_stride_h;
@@ -769,7 +793,7 @@ hipError_t launch_decode(const KernelArgs& k, const Plan& p, hipStream_t stream)
   a.mask_len = k.mask_len;
   if (k.query_start) a.query_len = k.dec_max_len;  // the longest query this launch serves
   const size_t lds = (size_t)p.bt_entries * sizeof(int32_t);
-  switch (k.head_dim) {
+  switch (instance_dim(k.head_dim)) {
     case 64: return launch_dim<64>(a, p, lds, stream);
     case 256: return launch_dim<256>(a, p, lds, stream);
     default: return launch_dim<128>(a, p, lds, stream);

@@ -18,7 +18,7 @@ struct KernelArgs {
   void* out;
   void* workspace;
   int batch, num_q_heads, num_kv_heads, query_len, num_pages, page_size, max_pages;
-  int head_dim = 128;  // 64, 128 or 256
+  int head_dim = 128;  // a multiple of 8 up to 256 (the row length of query, pages and out)
   float scale;
   int causal;
   uint32_t epoch;  // per-call tag of the arrival counters in the workspace (never 0)
@@ -54,7 +54,7 @@ struct AppendKernelArgs {
   const int32_t* block_table;
   const int32_t* context_lens;
   int batch, num_kv_heads, new_len, num_pages, page_size, max_pages;
-  int head_dim = 128;  // 64, 128 or 256
+  int head_dim = 128;  // a multiple of 8 up to 256
 };
 
 // Writes new tokens' K/V into their page slots (pa_append.hip).

@@ -35,7 +35,7 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
   if (s.num_q_heads % s.num_kv_heads != 0)
     return fail(err, kErrInvalid, "num_q_heads must be a multiple of num_kv_heads");
   if (!head_dim_supported(s.head_dim))
-    return fail(err, kErrUnsupported, "head_dim must be 64, 128 or 256");
+    return fail(err, kErrUnsupported, "head_dim must be a multiple of 8 from 8 to 256");
   const int64_t max_ctx = s.max_pages * s.page_size;
   if (max_ctx > INT32_MAX) return fail(err, kErrUnsupported, "max_pages * page_size exceeds int32");
   if (s.causal && max_ctx < s.query_len)
@@ -49,7 +49,7 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
   p.max_ctx = max_ctx;
   p.ps_log2 = log2_exact(s.page_size);
   const int64_t rows = int64_t(p.group) * s.query_len;
-  if (schedule == 0) schedule = rows <= kDecodeMaxRows ? kScheduleDecode : kSchedulePrefill;
+  if (schedule == 0) schedule = rows <= kDecodeAutoRows ? kScheduleDecode : kSchedulePrefill;
   p.schedule = schedule;
 
   if (schedule == kScheduleDecode) {
@@ -74,7 +74,7 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
     p.ws_ctr_offset = 0;
     p.ws_ml_offset = align_up(size_t(s.batch) * size_t(s.num_kv_heads) * sizeof(uint64_t), 256);
     p.ws_acc_offset = align_up(p.ws_ml_offset + slots * 2 * sizeof(float), 256);
-    p.workspace_bytes = align_up(p.ws_acc_offset + slots * size_t(s.head_dim) * sizeof(float), 256);
+    p.workspace_bytes = align_up(p.ws_acc_offset + slots * size_t(instance_dim(s.head_dim)) * sizeof(float), 256);
   } else {
     // rows of a work item: (position, query head) pairs of one kv head's group
     p.n_qtiles = int(cdiv(rows, kPrefillBlockM));
@@ -91,7 +91,8 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
       p.ws_ctr_offset = 0;
       p.ws_ml_offset = align_up(size_t(p.num_work) * sizeof(uint64_t), 256);
       p.ws_acc_offset = align_up(p.ws_ml_offset + parts * 2 * sizeof(float), 256);
-      p.workspace_bytes = align_up(p.ws_acc_offset + parts * size_t(s.head_dim) * sizeof(float), 256);
+      p.workspace_bytes =
+          align_up(p.ws_acc_offset + parts * size_t(instance_dim(s.head_dim)) * sizeof(float), 256);
     }
   }
   *plan = p;
@@ -111,14 +112,15 @@ int make_plan_varlen(const Shape& s, int decode_max_len, int decode_work_items, 
   if (decode_work_items < 0 || decode_work_items > kDecodeMaxWork)
     return fail(err, kErrInvalid, "decode_work_items must be in [0, 65536]");
   if (decode_max_len == -1) {
-    // Every query fits one decode work item: the uniform rule. Otherwise only
-    // one-token queries take the decode schedule: its cost grows with the
-    // rows of its widest sequence (2.2x from 4 to 8 rows, measured), so a
-    // 2-token query would slow every decode of the batch.
-    if (int64_t(group) * s.query_len <= kDecodeMaxRows)
+    // Every query fits the automatic decode bound: the uniform rule.
+    // Otherwise only one-token queries take the decode schedule, if their
+    // rows fit the bound: its cost grows with the rows of its widest sequence
+    // (2.2x from 4 to 8 rows, measured), so a 2-token query would slow every
+    // decode of the batch.
+    if (int64_t(group) * s.query_len <= kDecodeAutoRows)
       v.dec_max_len = int(s.query_len);
     else
-      v.dec_max_len = group <= kDecodeMaxRows ? 1 : 0;
+      v.dec_max_len = group <= kDecodeAutoRows ? 1 : 0;
   } else {
     if (int64_t(decode_max_len) * group > kDecodeMaxRows)
       return fail(err, kErrInvalid, "decode_max_len * num_q_heads / num_kv_heads must be <= 8");

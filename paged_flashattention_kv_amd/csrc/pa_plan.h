@@ -12,11 +12,22 @@
 
 namespace pa {
 
-// head dims the kernels implement
-constexpr bool head_dim_supported(int64_t d) { return d == 64 || d == 128 || d == 256; }
-// keys per decode wave step: 8 KB of K and V (two keys per lane, 16 dims each)
-constexpr int decode_step(int64_t head_dim) { return int(2048 / head_dim); }
+// Head dims the operator serves: any multiple of 8 from 8 to 256. 64, 128
+// and 256 have kernel instances of their own; any other runs the next larger
+// instance with the dims past it masked (zero query, no output stores).
+constexpr bool head_dim_supported(int64_t d) { return d >= 8 && d <= 256 && d % 8 == 0; }
+constexpr int instance_dim(int64_t d) { return d <= 64 ? 64 : d <= 128 ? 128 : 256; }
+// keys per decode wave step: 8 KB of K and V at the instance's head dim (two
+// keys per lane, 16 dims each)
+constexpr int decode_step(int64_t head_dim) { return int(2048 / instance_dim(head_dim)); }
 constexpr int kDecodeMaxRows = 8;    // q rows (GQA group x query_len) per decode work item
+// The automatic dispatch sends a query to the decode schedule while its rows
+// per kv head stay within kDecodeAutoRows. Measured over query lengths 1-16,
+// contexts 128-32768 and GQA 1, 4 and 8 (16 sequences, Qwen3-4B head
+// count): with 6 or 8 rows the tiled prefill schedule was faster at every
+// context (1.4-1.9x); with up to 4 rows the decode schedule wins once a call
+// streams several hundred MB of K/V, and it balances ragged batches.
+constexpr int kDecodeAutoRows = 4;
 constexpr int kDecodeWindow = 2048;  // keys whose block-table entries a decode work item stages at once
 constexpr int kDecodeAutoCap = 2048; // most decode work items the automatic choice launches
 constexpr int kDecodeMaxWork = 65536;

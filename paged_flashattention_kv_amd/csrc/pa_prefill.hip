@@ -40,7 +40,11 @@
 // XOR-swizzled by the key index so that both the K fragment reads and the V
 // transposed reads spread over the LDS banks. Head dims 64, 128 and 256 share
 // the code: D/16 contraction steps for Q K^T, D/32 output blocks for P V; at
-// 256 the four tile buffers take 128 KiB of LDS and one work item runs per CU. Aligned path
+// 256 the four tile buffers take 128 KiB of LDS and one work item runs per CU.
+// Any other multiple of 8 up to 256 (dv) runs the next larger instance: rows
+// are dv elements long in memory, query dims past dv are zero, LDS chunks
+// past dv are filled from the row's first chunk, and no output dim past dv
+// is stored. Aligned path
 // (page_size % 64 == 0): the tile is one contiguous span of one page, found
 // with a single table entry. Generic path: each key row is translated on
 // its own (tiles that cross pages). Keys at or past the context end read a
@@ -98,6 +102,7 @@ struct PrefillArgs {
   // query_len are served here. nullptr: uniform [B, H_q, query_len, 128].
   const int32_t* qstart;
   int total_query, skip_len;
+  int dv;  // head dim of query, pages and out (<= D: dims past it are masked)
   int batch, num_q_heads, num_kv_heads, query_len, group, n_qtiles;
   int page_size, ps_log2, max_pages;
   float c;         // |scale| * log2(e), > 0 (fold_scale)
@@ -145,6 +150,14 @@ __device__ __forceinline__ int swz(int key) {
   return ((key & 3) << 2) | ((key >> 2) & 3);
 }
 
+// The 16-byte chunk of a key row in memory that fills LDS chunk `chunk`: the
+// chunk itself, or the row's first chunk for a chunk past the head dim dv
+// (finite data that a zero query weights by 0 and no output dim stores).
+template <bool GEN>
+__device__ __forceinline__ int src_chunk(const PrefillArgs& a, int chunk) {
+  return !GEN || chunk * 8 < a.dv ? chunk : 0;
+}
+
 // Byte offset of (key, chunk) inside a tile buffer.
 template <int D>
 __device__ __forceinline__ int tile_off(int key, int chunk) { return key * (2 * D) + ((chunk ^ swz<D>(key)) << 4); }
@@ -159,7 +172,7 @@ struct TilePages {
 
 typedef __attribute__((address_space(4))) const int32_t constant_i32;
 
-template <bool ALIGNED, int D>
+template <bool ALIGNED, int D, bool GEN>
 __device__ __forceinline__ void lookup_tile(const PrefillArgs& a, const int32_t* bt_row, size_t page_stride,
                                             size_t head_off, int ctx, int t0, int wave, int lane,
                                             TilePages<ALIGNED, D>& tp) {
@@ -168,14 +181,14 @@ __device__ __forceinline__ void lookup_tile(const PrefillArgs& a, const int32_t*
     // one uniform entry per tile: a scalar load (the table is read-only here)
     const int lp = div_ps(t0, a.page_size, a.ps_log2);
     const int32_t page = ((constant_i32*)bt_row)[lp];
-    tp.row[0] = (size_t)page * page_stride + head_off + (size_t)(t0 - lp * a.page_size) * D;
+    tp.row[0] = (size_t)page * page_stride + head_off + (size_t)(t0 - lp * a.page_size) * (GEN ? a.dv : D);
   } else {
 #pragma unroll
     for (int i = 0; i < T::kInsts; ++i) {
       int key = t0 + 16 * wave + T::kRowsPerInst * i + lane / T::kChunks;
       key = key < ctx ? key : ctx - 1;  // past the context: re-read a valid row
       const int lp = div_ps(key, a.page_size, a.ps_log2);
-      tp.row[i] = (size_t)bt_row[lp] * page_stride + head_off + (size_t)(key - lp * a.page_size) * D;
+      tp.row[i] = (size_t)bt_row[lp] * page_stride + head_off + (size_t)(key - lp * a.page_size) * (GEN ? a.dv : D);
     }
   }
 }
@@ -188,7 +201,7 @@ __device__ __forceinline__ void lookup_tile(const PrefillArgs& a, const int32_t*
 // one page: a wave-uniform base (scalar registers) plus a per-lane byte
 // offset that is the same for every tile, so its loads cost no vector
 // arithmetic.
-template <bool ALIGNED, int D>
+template <bool ALIGNED, int D, bool GEN>
 __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages<ALIGNED, D>& tp, int ctx, int t0,
                                            int wave, int lane, char* kbuf, char* vbuf) {
   using T = Tile<D>;
@@ -198,8 +211,8 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages
 #pragma unroll
     for (int i = 0; i < T::kInsts; ++i) {
       const int key = 16 * wave + T::kRowsPerInst * i + lane / T::kChunks;  // key inside the tile
-      const int chunk = (lane % T::kChunks) ^ swz<D>(key);
-      const uint32_t off = (uint32_t)(key * D + chunk * 8) * 2u;  // bytes from the tile's first row
+      const int chunk = src_chunk<GEN>(a, (lane % T::kChunks) ^ swz<D>(key));
+      const uint32_t off = (uint32_t)(key * (GEN ? a.dv : D) + chunk * 8) * 2u;  // bytes from the tile's first row
       const int lds_off = wave * 32 * D + i * 1024;
       __builtin_amdgcn_global_load_lds((global_void*)(kbase + off), (lds_void*)(kbuf + lds_off), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((global_void*)(vbase + off), (lds_void*)(vbuf + lds_off), 16, 0, 0);
@@ -209,11 +222,11 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages
 #pragma unroll
   for (int i = 0; i < T::kInsts; ++i) {
     const int key = 16 * wave + T::kRowsPerInst * i + lane / T::kChunks;  // key inside the tile
-    const int chunk = (lane % T::kChunks) ^ swz<D>(key);
+    const int chunk = src_chunk<GEN>(a, (lane % T::kChunks) ^ swz<D>(key));
     size_t row;
     if (ALIGNED) {
       // the tile lies in one page; keys past the context re-read the tile's first row
-      row = tp.row[0] + (size_t)(t0 + key < ctx ? key : 0) * D;
+      row = tp.row[0] + (size_t)(t0 + key < ctx ? key : 0) * (GEN ? a.dv : D);
     } else {
       row = tp.row[i];
     }
@@ -292,7 +305,7 @@ __device__ __forceinline__ void lds_read_tr_pair(u32x4_t& f, uint32_t lo_addr, u
 
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <bool ALIGNED, int D, bool MASKED>
+template <bool ALIGNED, int D, bool MASKED, bool GEN>
 __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) pa_prefill_mfma(PrefillArgs a) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(1024))) char lds_k0[T::kBytes];
@@ -356,7 +369,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   const int pos = row_c / G;
   const int head = kvh * G + row_c % G;
 
-  const size_t head_stride = (size_t)a.page_size * D;
+  const size_t head_stride = (size_t)a.page_size * (GEN ? a.dv : D);
   const size_t page_stride = head_stride * a.num_kv_heads;
   const size_t head_off = (size_t)kvh * head_stride;
   const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
@@ -364,20 +377,21 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   // ---- first tile in flight before anything else ----
   TilePages<ALIGNED, D> tp;
   if (n_tiles > t_lo) {
-    lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, t_lo * kBN, wave, lane, tp);
-    issue_tile<ALIGNED, D>(a, tp, ctx, t_lo * kBN, wave, lane, lds_k0, lds_v0);
-    lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, min(t_lo + 1, n_tiles - 1) * kBN, wave, lane, tp);
+    lookup_tile<ALIGNED, D, GEN>(a, bt_row, page_stride, head_off, ctx, t_lo * kBN, wave, lane, tp);
+    issue_tile<ALIGNED, D, GEN>(a, tp, ctx, t_lo * kBN, wave, lane, lds_k0, lds_v0);
+    lookup_tile<ALIGNED, D, GEN>(a, bt_row, page_stride, head_off, ctx, min(t_lo + 1, n_tiles - 1) * kBN, wave, lane, tp);
   }
 
   // ---- Q^T operand: lane holds row r0 + col, dims 16ks + 8half .. +8 ----
   bf16x8_t qv[T::kKs];
   {
     const size_t qrow = a.qstart ? (size_t)(start + pos) * a.num_q_heads + head : ((size_t)b * a.num_q_heads + head) * L + pos;
-    const uint16_t* qp = a.query + qrow * D + 8 * half;
+    const uint16_t* qp = a.query + qrow * (GEN ? a.dv : D) + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < T::kKs; ++ks) {
+      // dims past dv stay zero, so their (re-read) key chunks add nothing
       u32x4_t w = u32x4_t{0u, 0u, 0u, 0u};
-      if (row_abs < R) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks) ^ a.qsign;
+      if (row_abs < R && (!GEN || 16 * ks + 8 * half < a.dv)) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks) ^ a.qsign;
       qv[ks] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
@@ -442,12 +456,12 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
           }
       }
     }
-    if (t + 1 < n_tiles) issue_tile<ALIGNED, D>(a, tp, ctx, t0 + kBN, wave, lane, knext, vnext);
+    if (t + 1 < n_tiles) issue_tile<ALIGNED, D, GEN>(a, tp, ctx, t0 + kBN, wave, lane, knext, vnext);
     // Lookup for tile t + 2 (clamped so that it is unconditional), done
     // after this tile's matrix work, not between the barrier and it.
     const int t_look = min(t + 2, n_tiles - 1) * kBN;
     if (!active) {
-      lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, t_look, wave, lane, tp);
+      lookup_tile<ALIGNED, D, GEN>(a, bt_row, page_stride, head_off, ctx, t_look, wave, lane, tp);
       return;
     }
 
@@ -580,7 +594,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[g % (kVA + 1)]),
                                                             __builtin_bit_cast(bf16x8_t, pw), acc_o[db], 0, 0, 0);
       }
-      lookup_tile<ALIGNED, D>(a, bt_row, page_stride, head_off, ctx, t_look, wave, lane, tp);
+      lookup_tile<ALIGNED, D, GEN>(a, bt_row, page_stride, head_off, ctx, t_look, wave, lane, tp);
   };
   for (int t = t_lo; t < n_tiles; t += 2) {
     tile_step(t, lds_k0, lds_v0, lds_k1, lds_v1);
@@ -596,12 +610,13 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
     const float inv = 1.f / l_tot;
     const size_t orow = a.qstart ? (size_t)(start + pos) * a.num_q_heads + head
                                  : ((size_t)b * a.num_q_heads + head) * L + pos;
-    uint16_t* op = a.out + orow * D;
+    uint16_t* op = a.out + orow * (GEN ? a.dv : D);
 #pragma unroll
     for (int db = 0; db < T::kDb; ++db) {
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         const int d0 = 32 * db + 8 * grp + 4 * half;
+        if (GEN && d0 >= a.dv) continue;  // a masked dim (dv is a multiple of 8)
         const u32x2_t w = {pack_bf16x2(acc_o[db][4 * grp] * inv, acc_o[db][4 * grp + 1] * inv),
                            pack_bf16x2(acc_o[db][4 * grp + 2] * inv, acc_o[db][4 * grp + 3] * inv)};
         *reinterpret_cast<u32x2_t*>(op + d0) = w;
@@ -685,7 +700,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
         const size_t orow =
             a.qstart ? (size_t)(start + pr / G) * a.num_q_heads + hr : ((size_t)b * a.num_q_heads + hr) * L + pr / G;
         const u32x2_t w = {pack_bf16x2(num.x / den, num.y / den), pack_bf16x2(num.z / den, num.w / den)};
-        *reinterpret_cast<u32x2_t*>(a.out + orow * D + d4) = w;
+        if (!GEN || d4 < a.dv) *reinterpret_cast<u32x2_t*>(a.out + orow * (GEN ? a.dv : D) + d4) = w;
       }
     }
   }
@@ -694,10 +709,12 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
 template <int D, bool MASKED>
 hipError_t launch_mask(const PrefillArgs& a, const Plan& p, hipStream_t stream) {
   const unsigned grid = (unsigned)(p.num_work * a.kv_splits);
-  if (p.aligned)
-    hipLaunchKernelGGL((pa_prefill_mfma<true, D, MASKED>), dim3(grid), dim3(kThreads), 0, stream, a);
+  if (a.dv != D)  // a head dim without an instance of its own: the next larger one, masked dims, per-row loader
+    hipLaunchKernelGGL((pa_prefill_mfma<false, D, MASKED, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  else if (p.aligned)
+    hipLaunchKernelGGL((pa_prefill_mfma<true, D, MASKED, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((pa_prefill_mfma<false, D, MASKED>), dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((pa_prefill_mfma<false, D, MASKED, false>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -732,6 +749,7 @@ hipError_t launch_prefill(const KernelArgs& k, const Plan& p, hipStream_t stream
   a.qstart = k.query_start;
   a.total_query = k.total_query;
   a.skip_len = k.query_start ? k.dec_max_len : 0;
+  a.dv = k.head_dim;
   a.mask = k.mask;
   a.msb = k.mask_stride_b;
   a.msh = k.mask_stride_h;
@@ -750,7 +768,7 @@ hipError_t launch_prefill(const KernelArgs& k, const Plan& p, hipStream_t stream
     a.ws_ml = reinterpret_cast<float*>(ws + p.ws_ml_offset);
     a.ws_acc = reinterpret_cast<float*>(ws + p.ws_acc_offset);
   }
-  switch (k.head_dim) {
+  switch (instance_dim(k.head_dim)) {
     case 64: return launch_dim<64>(a, p, stream);
     case 256: return launch_dim<256>(a, p, stream);
     default: return launch_dim<128>(a, p, stream);

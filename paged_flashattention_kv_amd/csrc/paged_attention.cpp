@@ -337,7 +337,8 @@ int paged_kv_append(const void* key_new, const void* value_new, void* key_pages,
   if (batch < 1 || num_kv_heads < 1 || new_len < 1 || head_dim < 1 || num_pages < 1 || page_size < 1 ||
       max_pages < 1)
     return set_error(PA_ERR_INVALID, "all sizes must be positive");
-  if (!pa::head_dim_supported(head_dim)) return set_error(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
+  if (!pa::head_dim_supported(head_dim))
+    return set_error(PA_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 from 8 to 256");
   const int64_t max_ctx = int64_t(max_pages) * page_size;
   if (max_ctx > INT32_MAX) return set_error(PA_ERR_UNSUPPORTED, "max_pages * page_size exceeds int32");
   if (max_ctx < new_len) return set_error(PA_ERR_INVALID, "max_pages * page_size < new_len");

@@ -29,7 +29,17 @@ int main() {
   // invalid sizes
   CHECK(pa::make_plan(shape(0, 32, 8, 1, 128, 16, 4), 0, 0, true, &p, &err) == pa::kErrInvalid);
   CHECK(pa::make_plan(shape(1, 30, 8, 1, 128, 16, 4), 0, 0, true, &p, &err) == pa::kErrInvalid);
-  CHECK(pa::make_plan(shape(1, 32, 8, 1, 96, 16, 4), 0, 0, true, &p, &err) == pa::kErrUnsupported);
+  CHECK(pa::make_plan(shape(1, 32, 8, 1, 100, 16, 4), 0, 0, true, &p, &err) == pa::kErrUnsupported);
+  CHECK(pa::make_plan(shape(1, 32, 8, 1, 264, 16, 4), 0, 0, true, &p, &err) == pa::kErrUnsupported);
+  CHECK(pa::make_plan(shape(1, 32, 8, 1, 0, 16, 4), 0, 0, true, &p, &err) == pa::kErrInvalid);
+  // head dims without an instance of their own run the next larger one (workspace sized for it)
+  for (int D : {8, 56, 72, 80, 96, 112, 136, 160, 192, 248}) {
+    CHECK(pa::make_plan(shape(2, 8, 2, 1, D, 16, 40), 0, 0, true, &p, &err) == pa::kOk);
+    CHECK(p.schedule == pa::kScheduleDecode && p.aligned == (16 % (2048 / pa::instance_dim(D)) == 0));
+    pa::Plan q;
+    CHECK(pa::make_plan(shape(2, 8, 2, 1, pa::instance_dim(D), 16, 40), 0, 0, true, &q, &err) == pa::kOk);
+    CHECK(p.workspace_bytes == q.workspace_bytes);
+  }
   CHECK(pa::make_plan(shape(1, 32, 8, 1, 512, 16, 4), 0, 0, true, &p, &err) == pa::kErrUnsupported);
   // other head dims: the decode step (8 KB of K and V per wave) and the workspace follow D
   for (int D : {64, 128, 256}) {
@@ -54,7 +64,7 @@ int main() {
   for (int L = 1; L <= 64; ++L) {
     for (int G : {1, 2, 4, 8}) {
       CHECK(pa::make_plan(shape(3, 8 * G, 8, L, 128, 16, 300), 0, 0, true, &p, &err) == pa::kOk);
-      CHECK(p.schedule == (G * L <= 8 ? pa::kScheduleDecode : pa::kSchedulePrefill));
+      CHECK(p.schedule == (G * L <= 4 ? pa::kScheduleDecode : pa::kSchedulePrefill));
       if (p.schedule == pa::kScheduleDecode) {
         CHECK(p.rows == G * L && p.rows_pad >= p.rows && p.rows_pad <= 8);
         CHECK(p.work_cap == pa::kDecodeAutoCap && p.work_items == 0);
@@ -118,7 +128,7 @@ int main() {
   for (int maxL : {1, 2, 3, 8, 65, 128, 2048}) {
     for (int G : {1, 2, 4, 8, 16}) {
       CHECK(pa::make_plan_varlen(shape(5, 8 * G, 8, maxL, 128, 16, 300), -1, 0, true, &v, &err) == pa::kOk);
-      const int want = G * maxL <= 8 ? maxL : (G <= 8 ? 1 : 0);
+      const int want = G * maxL <= 4 ? maxL : (G <= 4 ? 1 : 0);
       CHECK(v.dec_max_len == want);
       CHECK(v.run_decode == (want > 0) && v.run_prefill == (maxL > want));
       const size_t dec_ws = v.run_decode ? v.dec.workspace_bytes : 0;
@@ -148,7 +158,7 @@ int main() {
   CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 128, 128, 9), -1, -1, true, &v, &err) == pa::kErrInvalid);
   CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 128, 128, 9), -1, 70000, true, &v, &err) == pa::kErrInvalid);
   CHECK(pa::make_plan_varlen(shape(64, 30, 8, 128, 128, 128, 9), -1, 0, true, &v, &err) == pa::kErrInvalid);
-  CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 96, 128, 9), -1, 0, true, &v, &err) == pa::kErrUnsupported);
+  CHECK(pa::make_plan_varlen(shape(64, 32, 8, 128, 100, 128, 9), -1, 0, true, &v, &err) == pa::kErrUnsupported);
   // explicit decode work items reach the decode part
   CHECK(pa::make_plan_varlen(shape(4, 32, 8, 1, 128, 16, 9), -1, 5, true, &v, &err) == pa::kOk);
   CHECK(v.run_decode && !v.run_prefill && v.dec.work_items == 5 && v.dec.work_cap == 5);

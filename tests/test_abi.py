@@ -62,7 +62,7 @@ def _call(lib, **kw):
         (dict(L=200), native.PA_ERR_INVALID),
         (dict(causal=2), native.PA_ERR_INVALID),
         (dict(scale=float("nan")), native.PA_ERR_INVALID),
-        (dict(D=96), native.PA_ERR_UNSUPPORTED),
+        (dict(D=100), native.PA_ERR_UNSUPPORTED),
         (dict(D=512), native.PA_ERR_UNSUPPORTED),
         (dict(D=0), native.PA_ERR_INVALID),
         (dict(sched=7), native.PA_ERR_INVALID),
@@ -96,7 +96,7 @@ def _append(lib, **kw):
         (dict(B=0), native.PA_ERR_INVALID),
         (dict(L=0), native.PA_ERR_INVALID),
         (dict(ps=0), native.PA_ERR_INVALID),
-        (dict(D=96), native.PA_ERR_UNSUPPORTED),
+        (dict(D=100), native.PA_ERR_UNSUPPORTED),
         (dict(L=65, ps=16, mp=4), native.PA_ERR_INVALID),  # 65 new tokens cannot fit 4 pages of 16
         (dict(mp=1 << 20, ps=1 << 12), native.PA_ERR_UNSUPPORTED),  # positions past int32
         (dict(vp=FAKE + 0x200000 + 4096), native.PA_ERR_INVALID),  # the two pools overlap
@@ -131,7 +131,7 @@ def _varlen(lib, **kw):
         (dict(Hq=3), native.PA_ERR_INVALID),
         (dict(causal=2), native.PA_ERR_INVALID),
         (dict(scale=float("inf")), native.PA_ERR_INVALID),
-        (dict(D=96), native.PA_ERR_UNSUPPORTED),
+        (dict(D=100), native.PA_ERR_UNSUPPORTED),
         (dict(dml=5), native.PA_ERR_INVALID),  # 5 rows x group 2 > 8
         (dict(dml=-2), native.PA_ERR_INVALID),
         (dict(split=-1), native.PA_ERR_INVALID),
@@ -165,7 +165,7 @@ def _masked(lib, **kw):
         (dict(sl=-64), native.PA_ERR_INVALID),
         (dict(mlen=0), native.PA_ERR_INVALID),
         (dict(sh=1 << 41), native.PA_ERR_UNSUPPORTED),
-        (dict(D=96), native.PA_ERR_UNSUPPORTED),
+        (dict(D=100), native.PA_ERR_UNSUPPORTED),
         (dict(q=None), native.PA_ERR_INVALID),
         (dict(out=FAKE + 0x600000 + 128), native.PA_ERR_INVALID),  # out inside the mask
         (dict(sched=0), native.PA_ERR_WORKSPACE),  # decode schedule without workspace
@@ -185,9 +185,13 @@ def test_varlen_workspace(lib):
     # a prefill chunk in the batch: only one-token queries take the decode part
     n = native.varlen_workspace_bytes(64, 32, 8, 128, 128, 128, 9)
     assert n == native.workspace_bytes(64, 32, 8, 1, 128, 128, 9, native.SCHEDULE_DECODE, 0)
-    # every query short enough for one decode work item: the uniform rule
-    assert native.varlen_workspace_bytes(64, 32, 8, 2, 128, 128, 9) == native.workspace_bytes(64, 32, 8, 2, 128, 128, 9)
+    # every query within the automatic decode bound (4 rows per kv head): the uniform rule
     assert native.varlen_workspace_bytes(64, 32, 8, 1, 128, 128, 9) == native.workspace_bytes(64, 32, 8, 1, 128, 128, 9)
+    assert native.varlen_workspace_bytes(64, 32, 16, 2, 128, 128, 9) == native.workspace_bytes(
+        64, 32, 16, 2, 128, 128, 9) > 0
+    # 2-token queries at GQA 4 (8 rows) take the prefill schedule; one-token ones the decode part
+    assert native.varlen_workspace_bytes(64, 32, 8, 2, 128, 128, 9) == native.workspace_bytes(
+        64, 32, 8, 1, 128, 128, 9, native.SCHEDULE_DECODE, 0)
     assert native.varlen_workspace_bytes(64, 32, 8, 128, 128, 128, 9, decode_max_len=0) == 0
     # group 16: no decode part; 256 prefill work items (16 heads x 128 positions = 2048 rows
     # per kv head) take the key-range split, whose workspace is the uniform prefill's
@@ -199,9 +203,11 @@ def test_varlen_workspace(lib):
 
 def test_schedule_rule_and_workspace(lib):
     assert native.schedule_for(64, 32, 8, 1, 128, 128, 33) == native.SCHEDULE_DECODE
-    assert native.schedule_for(64, 32, 8, 2, 128, 128, 33) == native.SCHEDULE_DECODE
+    assert native.schedule_for(64, 32, 8, 2, 128, 128, 33) == native.SCHEDULE_PREFILL  # 8 rows per kv head
+    assert native.schedule_for(64, 32, 16, 2, 128, 128, 33) == native.SCHEDULE_DECODE  # 4 rows
     assert native.schedule_for(64, 32, 8, 3, 128, 128, 33) == native.SCHEDULE_PREFILL
-    assert native.schedule_for(1, 8, 8, 8, 128, 128, 33) == native.SCHEDULE_DECODE
+    assert native.schedule_for(1, 8, 8, 4, 128, 128, 33) == native.SCHEDULE_DECODE
+    assert native.schedule_for(1, 8, 8, 8, 128, 128, 33) == native.SCHEDULE_PREFILL
     assert native.schedule_for(4, 32, 8, 2048, 128, 128, 16) == native.SCHEDULE_PREFILL
     assert native.workspace_bytes(4, 32, 8, 2048, 128, 128, 16) == 0
     # decode: arrival counters plus two partial (max, sum, acc[D]) slots per work item and row

@@ -337,10 +337,10 @@ def test_planted_mistake_is_caught(monkeypatch, mistake):
     assert not _pins_pass()
 
 
-@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("D", [8, 64, 80, 96, 112, 192, 256])
 @pytest.mark.parametrize("causal", [True, False])
 def test_other_head_dims_match_brute_force(D, causal):
-    # the definition has no head-dim-specific step; pin it at the two other supported head dims
+    # the definition has no head-dim-specific step; pin it at the other head dims the operator serves
     p = wl.make_problem(seed=90 + D, batch=2, num_q_heads=4, num_kv_heads=2, query_len=3, head_dim=D,
                         page_size=4, context_lens=[5, 9], causal=causal, poison=True)
     np.testing.assert_allclose(_ref(p), _brute(p), rtol=1e-12, atol=1e-12)
