@@ -11,10 +11,14 @@
 // Work division (HBM-bound; no matrix cores): the decode work is the sum of
 // the context lengths times the kv heads. It is cut into 64-key granules,
 // laid out segment by segment (segment = one (sequence, kv head) pair, in
-// sequence-major order), and the granule range is split evenly over a fixed
-// number of work items -- as many 256-thread work items as the GPU keeps
-// resident at once -- so every work item streams the same number of bytes
-// whatever the mix of context lengths. A work item walks its contiguous
+// sequence-major order), and the granule range is split over a fixed number
+// of work items -- as many 256-thread work items as the GPU keeps resident
+// at once -- by a cost model: every granule costs the same, a segment start
+// (a new piece, with its fixed latency) costs a few granules more, and the
+// second workgroup on each CU (served after the first) gets a smaller share,
+// so every work item streams for about the same time whatever the mix of
+// context lengths. The split is a deterministic function of the context
+// lengths, so results are bit-reproducible. A work item walks its contiguous
 // range piece by piece (a piece = the part of one segment inside the range).
 // A piece that is a whole segment is normalised and stored directly; a
 // piece of a segment shared with other work items (at most the first and
@@ -86,6 +90,18 @@ constexpr float kTau = 8.0f;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
 constexpr int kGran = 64;    // keys per granule: work ranges start and end on granules
+// The work split's cost model (see WorkSplit): a segment start costs 4
+// granules, and the grid's second half gets 12/16 of the first half's share.
+// Measured on the decode batch (per-workgroup timestamps): a piece costs 6-8
+// us of fixed latency (about 3 granules of streaming) and the second
+// workgroup on a CU streams ~18% slower; with the even split the last work
+// items (five pieces, second half) ended 25-30 us after the median. A/B on one
+// MI355X: decode batch 115.6 -> 107.8 us; long-context decode 333.5 -> 341.2
+// us (its segments are long and uniform, so it gains nothing and pays the
+// skew).
+constexpr int kSplitPieceCost = 4;  // granules a segment start costs in the work split
+constexpr int kSplitWa = 16;        // weight of the grid's first half
+constexpr int kSplitWb = 12;        // weight of the grid's second half
 constexpr int kWindow = 2048;  // keys per block-table staging window
 
 struct DecodeArgs {
@@ -342,8 +358,119 @@ __device__ __forceinline__ size_t row_idx(const DecodeArgs& a, int b, int start,
   return a.qstart ? (size_t)(start + l) * a.num_q_heads + h : ((size_t)b * a.num_q_heads + h) * L + l;
 }
 
-// Work item w covers granules [w * total / work_items, (w + 1) * total / work_items).
-__device__ __forceinline__ int64_t gran_begin(int64_t w, int64_t total, int64_t items) { return w * total / items; }
+// A value every lane of the wave holds, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// ---- the split of the work over the grid ----
+//
+// The work is laid out in granules, segment by segment (segment = one
+// (sequence, kv head), sequence-major), and split over the work items by
+// cost: a granule costs 1, and the start of a segment costs `c` more -- the
+// fixed latency of a piece (query rows, block-table window, pipeline fill,
+// partial store and arrival), so a work item whose range crosses many segment
+// boundaries gets fewer granules. The second half of the grid -- with two
+// resident workgroups per CU, the second one on each CU, whose waves the SIMD
+// serves after the first's -- gets weight wb against wa for the first half.
+// Granule g belongs to the work item whose cost range holds g's last cost
+// unit; every work item computes the same split from the same prefix, so the
+// pieces, partial slots and merges are the same on every run.
+struct WorkSplit {
+  int64_t T;     // granules
+  int64_t C;     // cost units: T + c * segments
+  int32_t P, H;  // work items; size of the first half (H = P: one weight for all)
+  int32_t Wt;    // kSplitWa * H + kSplitWb * (P - H)
+  int32_t c;     // cost of a segment start (0: an even split of granules)
+};
+
+// floor(num / den) for 0 <= num, 0 < den: a double-precision estimate
+// corrected with integer products (a 64-bit integer division is a long
+// emulated sequence; the estimate is exact or one off for num < 2^53).
+__device__ __forceinline__ int64_t div_floor(int64_t num, int64_t den) {
+  int64_t q = (int64_t)((double)num / (double)den);
+  while (q > 0 && q * den > num) --q;
+  while ((q + 1) * den <= num) ++q;
+  return q;
+}
+
+// Weight of the work items before w.
+__device__ __forceinline__ int64_t weight_before(const WorkSplit& s, int64_t w) {
+  return (int64_t)kSplitWa * min(w, (int64_t)s.H) + (int64_t)kSplitWb * max(w - s.H, (int64_t)0);
+}
+
+// First cost unit of work item w: floor(C * weight_before(w) / Wt).
+__device__ __forceinline__ int64_t cost_begin(const WorkSplit& s, int64_t w) {
+  return w >= s.P ? s.C : div_floor(s.C * weight_before(s, w), s.Wt);
+}
+
+// The work item whose cost range holds cost unit x (0 <= x < C): the largest
+// w with cost_begin(w) <= x, i.e. with weight_before(w) <= K =
+// floor(((x + 1) * Wt - 1) / C).
+__device__ __forceinline__ int64_t item_of_cost(const WorkSplit& s, int64_t x) {
+  const int64_t K = div_floor((x + 1) * s.Wt - 1, s.C);
+  const int64_t ha = (int64_t)kSplitWa * s.H;
+  const int64_t w = K < ha ? K / kSplitWa : s.H + (K - ha) / kSplitWb;
+  return min(w, (int64_t)s.P - 1);
+}
+
+// Granule that cost unit x of sequence b maps to (0 <= x - cp < the
+// sequence's cost): the first granule whose last cost unit is at or past x.
+// gp = granules per kv head before b, cp = cost units before b, ng = b's
+// granules per kv head. Work item w holds the granules from the one that
+// cost_begin(w) maps to up to the one that cost_begin(w + 1) maps to.
+__device__ __forceinline__ int64_t granule_of(const WorkSplit& s, int64_t x, int64_t gp, int64_t cp, int64_t ng,
+                                              int64_t hk) {
+  const int64_t seg = ng + s.c, rel = x - cp;  // rel < hk * seg
+  int64_t kvh;
+  if (rel < ((int64_t)1 << 32) && seg < ((int64_t)1 << 32))
+    kvh = (int64_t)((uint32_t)rel / (uint32_t)seg);
+  else
+    kvh = rel / seg;
+  const int64_t off = rel - kvh * seg;
+  return gp * hk + kvh * ng + max(off - s.c, (int64_t)0);
+}
+
+// The split for this launch: the cost terms only when every work item still
+// gets at least one granule (each range longer than a segment start's cost),
+// else the even split of granules.
+__device__ __forceinline__ WorkSplit make_split(const DecodeArgs& a, int64_t gran_per_head, int64_t nonempty) {
+  WorkSplit s;
+  s.T = gran_per_head * a.num_kv_heads;
+  s.P = a.work_items;
+  s.H = s.P / 2;
+  s.c = kSplitPieceCost;
+  s.C = s.T + (int64_t)s.c * nonempty * a.num_kv_heads;
+  s.Wt = kSplitWa * s.H + kSplitWb * (s.P - s.H);
+  const bool ok = s.T >= s.P && s.P >= 2 && s.C * min(kSplitWa, kSplitWb) >= (int64_t)(s.c + 2) * s.Wt;
+  if (!ok) {  // the even split: one weight, no cost terms
+    s.c = 0;
+    s.C = s.T;
+    s.H = s.P;
+    s.Wt = kSplitWa * s.P;
+  }
+  return s;
+}
+
+// The work items holding pieces of segment [S, E) (granules; its first cost
+// unit is CS) and the number of non-empty ones. With at least as many
+// granules as work items every work item holds one or more granules; with
+// fewer (even split), every non-empty work item holds exactly one, so the
+// segment's E - S granules sit in E - S work items.
+struct SegmentItems {
+  int64_t wf, wl;
+  uint32_t count;
+};
+
+__device__ __forceinline__ SegmentItems segment_items(const WorkSplit& s, int64_t S, int64_t E, int64_t CS) {
+  SegmentItems it;
+  it.wf = item_of_cost(s, CS + s.c);              // work item holding granule S
+  it.wl = item_of_cost(s, CS + s.c + (E - S) - 1);  // work item holding granule E - 1
+  it.count = (uint32_t)(s.T >= s.P ? it.wl - it.wf + 1 : E - S);
+  return it;
+}
 
 // One piece: keys [k0, k1) of segment (b, kvh), for the group * L query
 // rows of that kv head (sequence b has L rows from token `start`). Merges
@@ -520,23 +647,6 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
   }
 }
 
-// The work items holding pieces of segment [S, E) (granules) and the number
-// of non-empty ones. With at least as many granules as work items every work
-// item holds one or more granules; with fewer, every non-empty work item holds
-// exactly one, so the segment's E - S granules sit in E - S work items.
-struct SegmentItems {
-  int64_t wf, wl;
-  uint32_t count;
-};
-
-__device__ __forceinline__ SegmentItems segment_items(int64_t S, int64_t E, int64_t total, int64_t P) {
-  SegmentItems it;
-  it.wf = ((S + 1) * P - 1) / total;  // work item holding granule S
-  it.wl = (E * P - 1) / total;        // work item holding granule E - 1
-  it.count = (uint32_t)(total >= P ? it.wl - it.wf + 1 : E - S);
-  return it;
-}
-
 // Combines the partial states of one shared segment ("Week 2 Day 5", Task 2:
 // common maximum, one rescale factor per partial, one denominator, the head
 // dimensions in parallel). Work item w's piece sits in slot 0 when the
@@ -548,9 +658,8 @@ __device__ __forceinline__ SegmentItems segment_items(int64_t S, int64_t E, int6
 constexpr int kMergeBatch = 8;
 
 template <int D, bool GEN>
-__device__ void merge_segment(const DecodeArgs& a, int32_t* lds_parts, int b, int kvh, int L, int start, int64_t S,
-                              const SegmentItems& it, int64_t total) {
-  const int64_t P = a.work_items;
+__device__ void merge_segment(const DecodeArgs& a, int32_t* lds_parts, int b, int kvh, int L, int start, int64_t CS,
+                              const SegmentItems& it, const WorkSplit& sp) {
   const int n_rd = a.group * L * D;
   const int64_t n_w = it.wl - it.wf + 1;
   const int tid = threadIdx.x;
@@ -563,9 +672,14 @@ __device__ void merge_segment(const DecodeArgs& a, int32_t* lds_parts, int b, in
       const int nc = (int)min((int64_t)kThreads, n_w - c0);
       __syncthreads();  // the previous list is no longer read
       if (tid < nc) {
+        // The segment is w's first piece (slot 0) when w's cost range starts at
+        // or after the segment's first cost unit CS, else w's last piece (slot 1).
+        // With c = 0 a cost unit is a granule and a range may be empty; with
+        // c > 0 every range holds a granule.
         const int64_t w = it.wf + c0 + tid;
-        const int64_t gw = gran_begin(w, total, P);
-        lds_parts[tid] = gw < gran_begin(w + 1, total, P) ? (int)(w * 2 + (gw >= S ? 0 : 1)) : -1;
+        const int64_t xw = cost_begin(sp, w);
+        const bool empty = sp.c == 0 && xw == cost_begin(sp, w + 1);
+        lds_parts[tid] = empty ? -1 : (int)(w * 2 + (xw >= CS ? 0 : 1));
       }
       __syncthreads();
       for (int j0 = 0; j0 < nc; j0 += kMergeBatch) {
@@ -608,28 +722,32 @@ __device__ void merge_segment(const DecodeArgs& a, int32_t* lds_parts, int b, in
   }
 }
 
+// Two resident workgroups per CU (a register budget of 256 per lane) for the
+// instances that fit it; the 8-row and masked ones take one.
 template <int ROWS, bool ALIGNED, int D, bool MASKED, bool GEN>
-__global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
-  // With two resident workgroups per CU the second half of the grid is the
-  // second workgroup on each CU, whose waves the memory pipeline serves after
-  // the first's; a higher issue priority for them narrows that gap (measured
-  // 1% on a whole launch). Priority changes only the order of issue.
-  if (blockIdx.x >= gridDim.x / 2) __builtin_amdgcn_s_setprio(1);
+__global__ void __launch_bounds__(kThreads, (ROWS <= 4 && !MASKED) ? 2 : 1) pa_decode_work(DecodeArgs a) {
   extern __shared__ int32_t lds_bt[];
   __shared__ float lds_m[kWaves][ROWS];
   __shared__ float lds_l[kWaves][ROWS];
   __shared__ float lds_acc[kWaves][ROWS][D];
+  // granules per kv head (low 40 bits) and non-empty sequences (high 24 bits),
+  // inclusive over thread chunks
   __shared__ int64_t lds_scan[kThreads];
-  __shared__ int64_t lds_start[2];  // (sequence holding the first granule, its granule prefix)
+  __shared__ int64_t lds_start[5];  // sequence holding this item's first cost unit, its prefixes, G0, G1
   __shared__ int32_t lds_parts[kThreads];  // partial slots of the segment being merged
   __shared__ bool lds_last;
+  constexpr int kZShift = 40;
+  const int64_t kGMask = ((int64_t)1 << kZShift) - 1;
 
   const int tid = threadIdx.x;
   // ---- granule prefix over sequences: thread t sums a contiguous chunk ----
   const int chunk = (a.batch + kThreads - 1) / kThreads;
   const int c0 = min(a.batch, tid * chunk), c1 = min(a.batch, c0 + chunk);
   int64_t mine = 0;
-  for (int b = c0; b < c1; ++b) mine += seq_gran(a, b);
+  for (int b = c0; b < c1; ++b) {
+    const int64_t ng = seq_gran(a, b);
+    mine += ng + (ng > 0 ? (int64_t)1 << kZShift : 0);
+  }
   lds_scan[tid] = mine;
   __syncthreads();
   for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan
@@ -638,29 +756,40 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
     lds_scan[tid] += v;
     __syncthreads();
   }
-  const int64_t total_b = lds_scan[kThreads - 1];  // granules per kv head, all sequences
-  const int64_t total = total_b * a.num_kv_heads;
-  const int64_t excl = lds_scan[tid] - mine;
+  // every lane computes the same split: scalar registers
+  const int64_t all = uniform64(lds_scan[kThreads - 1]);
+  const WorkSplit sp = make_split(a, all & kGMask, all >> kZShift);
+  const int64_t hk = a.num_kv_heads;
   const int64_t w = blockIdx.x;
-  const int64_t G0 = gran_begin(w, total, a.work_items);
-  const int64_t G1 = gran_begin(w + 1, total, a.work_items);
+  const int64_t x0 = cost_begin(sp, w), x1 = cost_begin(sp, w + 1);
   {
-    // which sequence holds granule G0
-    int64_t pref = excl;
+    // which sequences hold cost units x0 (this item's first) and x1 (the next
+    // item's first): each thread checks its own chunk of sequences
+    const int64_t ex = lds_scan[tid] - mine;
+    int64_t gp = ex & kGMask, cp = hk * (gp + sp.c * (ex >> kZShift));
     for (int b = c0; b < c1; ++b) {
       const int64_t ng = seq_gran(a, b);
-      if (G0 >= pref * a.num_kv_heads && G0 < (pref + ng) * a.num_kv_heads) {
+      const int64_t cb = ng > 0 ? hk * (ng + sp.c) : 0;
+      if (x0 >= cp && x0 < cp + cb) {
         lds_start[0] = b;
-        lds_start[1] = pref;
+        lds_start[1] = gp;
+        lds_start[2] = cp;
+        lds_start[3] = granule_of(sp, x0, gp, cp, ng, hk);
       }
-      pref += ng;
+      if (x1 >= cp && x1 < cp + cb) lds_start[4] = granule_of(sp, x1, gp, cp, ng, hk);
+      gp += ng;
+      cp += cb;
     }
   }
   __syncthreads();
+  // a cost unit past the end (no work in this launch, or the last item's end) maps to T
+  const int64_t G0 = x0 >= sp.C ? sp.T : uniform64(lds_start[3]);
+  const int64_t G1 = x1 >= sp.C ? sp.T : uniform64(lds_start[4]);
   if (G0 >= G1) return;  // no work for this item (uniform)
 
-  int b = (int)lds_start[0];
-  int64_t pref = lds_start[1];
+  int b = (int)uniform64(lds_start[0]);
+  int64_t pref = uniform64(lds_start[1]);   // granules per kv head before sequence b
+  int64_t cpref = uniform64(lds_start[2]);  // cost units before sequence b
   int64_t G = G0;
   int nth = 0;
   while (G < G1) {
@@ -683,18 +812,21 @@ __global__ void __launch_bounds__(kThreads) pa_decode_work(DecodeArgs a) {
                                    nth == 0 ? 0 : 1);
     if (!direct) {
       // publish this piece, then the last of the segment's work items merges it
+      // (CS: the segment's first cost unit)
+      const int64_t CS = cpref + kvh * (ng + (int64_t)sp.c);
+      const SegmentItems it = segment_items(sp, S, E, CS);
       wait_stores();
       __syncthreads();
-      const SegmentItems it = segment_items(S, E, total, a.work_items);
       if (tid == 0) lds_last = arrive_last(a.ws_ctr + (size_t)b * a.num_kv_heads + kvh, a.epoch, it.count);
       __syncthreads();
-      if (lds_last) merge_segment<D, GEN>(a, lds_parts, b, kvh, L, start, S, it, total);
+      if (lds_last) merge_segment<D, GEN>(a, lds_parts, b, kvh, L, start, CS, it, sp);
     }
     G = gend;
     ++nth;
     if (G == base + (int64_t)a.num_kv_heads * ng) {  // past the last kv head of sequence b
       ++b;
       pref += ng;
+      cpref += (int64_t)a.num_kv_heads * (ng + (int64_t)sp.c);
     }
   }
 }
