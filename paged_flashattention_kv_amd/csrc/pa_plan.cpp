@@ -82,12 +82,13 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
     p.num_work = int64_t(p.n_qtiles) * s.num_kv_heads * s.batch;
     if (p.num_work > INT32_MAX) return fail(err, kErrUnsupported, "prefill grid too large");
     if (p.num_work < kPrefillSplitTarget) {
-      int64_t splits = std::min<int64_t>(kPrefillMaxSplits, kPrefillSplitTarget / p.num_work);
-      splits = std::min<int64_t>(splits, max_ctx / (2 * kPrefillBlockN));  // two tiles per part at least
+      // room for up to kPrefillMaxSplits parts per work item (the kernel picks each item's count)
+      const int64_t splits = std::min<int64_t>(kPrefillMaxSplits, max_ctx / (2 * kPrefillBlockN));
       p.kv_splits = int(std::max<int64_t>(splits, 1));
     }
     if (p.kv_splits > 1) {
-      const size_t parts = size_t(p.num_work) * size_t(p.kv_splits) * kPrefillBlockM;
+      // one entry per workgroup of the split launch: kPrefillSplitTarget parts at most
+      const size_t parts = size_t(kPrefillSplitTarget) * kPrefillBlockM;
       p.ws_ctr_offset = 0;
       p.ws_ml_offset = align_up(size_t(p.num_work) * sizeof(uint64_t), 256);
       p.ws_acc_offset = align_up(p.ws_ml_offset + parts * 2 * sizeof(float), 256);

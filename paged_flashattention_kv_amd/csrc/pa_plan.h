@@ -34,11 +34,13 @@ constexpr int kDecodeMaxWork = 65536;
 constexpr int kPrefillBlockM = 128;  // packed (position, query head) rows per prefill work item
 constexpr int kPrefillBlockN = 64;   // keys per prefill K/V tile
 // A prefill launch with fewer work items than kPrefillSplitTarget (two per CU
-// on a 256-CU part) splits every work item's key range into up to
-// kPrefillMaxSplits parts of at least two tiles each, merged through the
-// workspace.
+// on a 256-CU part) splits the work items' key ranges into parts of about
+// equal length, merged through the workspace: the kernel picks the shortest
+// part length at which all parts fit the resident workgroups (at most
+// kPrefillSplitTarget) and gives each work item as many parts as its own
+// length calls for (at most kPrefillMaxSplits, at least two tiles each).
 constexpr int kPrefillSplitTarget = 512;
-constexpr int kPrefillMaxSplits = 4;
+constexpr int kPrefillMaxSplits = 8;
 constexpr int kScheduleDecode = 1;
 constexpr int kSchedulePrefill = 2;
 
@@ -67,8 +69,8 @@ struct Plan {
   // decode: arrival counters [B * H_kv] u64 (zero-filled before first use),
   // partial (max, sum) [work_cap][2][rows][2] f32, partial outputs
   // [work_cap][2][rows][D] f32. Split prefill: counters [num_work] u64,
-  // (max, sum) [num_work][kv_splits][128][2] f32, outputs
-  // [num_work][kv_splits][128][D] f32.
+  // (max, sum) [kPrefillSplitTarget][128][2] f32, outputs
+  // [kPrefillSplitTarget][128][D] f32.
   size_t ws_ctr_offset = 0;
   size_t ws_ml_offset = 0;
   size_t ws_acc_offset = 0;

@@ -115,14 +115,17 @@ struct PrefillArgs {
   int64_t msb, msh, msl;
   int mask_len;
   int mask_vec;  // every mask row starts 16-byte aligned: four keys per load
-  // Split key range: work item i's part s (s < kv_splits) covers tiles
-  // [s * n / kv_splits, (s + 1) * n / kv_splits) of its n tiles and leaves
-  // its rows' (reference max, row sum, unnormalised output) in slot
-  // i * kv_splits + s; the part that arrives last at counter i merges them.
+  // Split key range (kv_splits > 1): work item i runs in p_i parts (1 <=
+  // p_i <= kv_splits, from its length and the launch's total, see
+  // split_assign); part s < p_i covers tiles [s * n / p_i, (s + 1) * n /
+  // p_i) of its n tiles and leaves its rows' (reference max, row sum,
+  // unnormalised output) in a workspace entry of its own; the part that
+  // arrives last at counter i merges them.
   int num_work, kv_splits;
+  int split_slots;   // resident workgroups of this kernel instance, at most kPrefillSplitTarget
   uint64_t* ws_ctr;  // [num_work] arrival counters (epoch << 32 | count)
-  float* ws_ml;      // [num_work * kv_splits][128][2]
-  float* ws_acc;     // [num_work * kv_splits][128][D]
+  float* ws_ml;      // [kPrefillSplitTarget][128][2]
+  float* ws_acc;     // [kPrefillSplitTarget][128][D]
   uint32_t epoch;
 };
 
@@ -305,6 +308,145 @@ __device__ __forceinline__ void lds_read_tr_pair(u32x4_t& f, uint32_t lo_addr, u
 
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Key tiles a work item of row tile `rtile` of a sequence with L query rows
+// and context ctx streams (the whole-tile causal skip included).
+__device__ __forceinline__ int item_tiles(const PrefillArgs& a, int rtile, int L, int ctx) {
+  const int R = a.group * L;
+  const int tile_last_pos = (min(rtile * kBM + kBM, R) - 1) / a.group;
+  const int kv_end = a.causal ? min(ctx, tile_last_pos + ctx - L + 1) : ctx;
+  return (kv_end + kBN - 1) / kBN;
+}
+
+// What a workgroup of a split launch runs: part `part` of the n_parts of
+// work item `item` (item < 0: nothing), its partial state in workspace
+// entry (u0 + part) * num_kv_heads + kv head.
+struct SplitItem {
+  int item, part, n_parts, u0;
+};
+
+// Parts of a pair with nt key tiles (nt < 0: no rows, no part) at part
+// length T: clamp(ceil(nt / T), 1, min(cap, nt / 2)), without branches.
+// capT = cap * T, rT ~ 1 / T. ceil is taken of min(nt, capT) / T, which is
+// at most cap and equal to cap when nt > capT; for it a single-precision
+// estimate is off by one at most and one integer step corrects it.
+__device__ __forceinline__ int pair_parts(int nt, int T, int cap, int capT, float rT) {
+  const int y = min(nt, capT) + T - 1;
+  int q = (int)((float)y * rT);
+  q -= q * T > y ? 1 : 0;
+  q += (q + 1) * T <= y ? 1 : 0;
+  const int p = max(1, min(q, min(cap, nt >> 1)));
+  return nt < 0 ? 0 : p;
+}
+
+// Assignment of a split launch's workgroups, the same in every workgroup.
+// The (sequence, row tile) pairs are taken in work-item order, heavy row
+// tiles first: pair o is row tile n_qtiles - 1 - o / batch of sequence
+// o % batch, and streams n_o key tiles. The part length T (in tiles) is the
+// smallest for which
+//   H_kv * sum_o parts(n_o, T) <= a.split_slots,
+//   parts(n, T) = clamp(ceil(n / T), 1, min(kv_splits, n / 2)),
+// searched over 256 candidates in parallel (one per thread) from
+// ceil(total / slots) to the longest pair (where every pair has one part),
+// so that every part is resident at once and the longest sequences do not
+// set the time. The parts are listed pair by pair, each once per kv head:
+// workgroup w runs the u-th listed part, u = w / H_kv, for kv head w % H_kv
+// (with 8 kv heads every part of a kv head lands on one XCD and shares its
+// L2); workgroups past the list run nothing. Called by every thread
+// (barriers inside); there are fewer pairs than kPrefillSplitTarget.
+__device__ SplitItem split_assign(const PrefillArgs& a, int* lds_n, int64_t* lds_sum, int* lds_red) {
+  const int nq = a.n_qtiles;
+  const int pairs = a.batch * nq;
+  const int pairs4 = (pairs + 3) & ~3;  // padded with empty pairs for 4-wide reads
+  int64_t sum = 0;
+  int longest = 0;
+  for (int o = threadIdx.x; o < pairs4; o += kThreads) {
+    int t = -1;  // no rows: no part
+    if (o < pairs) {
+      const int b = o % a.batch, r = nq - 1 - o / a.batch;
+      int L = a.query_len;
+      bool live = true;
+      if (a.qstart) {
+        const int s0 = a.qstart[b], s1 = a.qstart[b + 1];
+        const int64_t len = (int64_t)s1 - s0;
+        live = !(s0 < 0 || s1 > a.total_query || len <= a.skip_len || len > a.query_len);
+        L = live ? (int)len : 0;
+      }
+      if (live && r * kBM < a.group * L) t = max(0, item_tiles(a, r, L, a.context_lens[b]));
+    }
+    lds_n[o] = t;
+    sum += max(t, 0);
+    longest = max(longest, t);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    sum += __shfl_xor(sum, m);
+    longest = max(longest, __shfl_xor(longest, m));
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) {
+    lds_sum[w] = sum;
+    lds_red[w] = longest;
+  }
+  __syncthreads();
+  const int H = a.num_kv_heads;
+  const int64_t total = (lds_sum[0] + lds_sum[1] + lds_sum[2] + lds_sum[3]) * H;
+  const int hi = max(1, max(max(lds_red[0], lds_red[1]), max(lds_red[2], lds_red[3])));
+  // ceil(total / slots) in double precision (exact below 2^53, no 64-bit integer division)
+  const int lo = (int)fmin((double)hi, fmax(2.0, ceil((double)total / (double)a.split_slots)));
+  const int step = max(1, (hi - lo + kThreads - 2) / (kThreads - 1));
+  const int cap = a.kv_splits;
+  {
+    const int cand = threadIdx.x == kThreads - 1 ? hi : min(hi, lo + (int)threadIdx.x * step);
+    const float rc = 1.0f / (float)cand;
+    const int capc = cap * cand;
+    int count = 0;  // at most cap * pairs
+#pragma unroll 2
+    for (int o = 0; o < pairs4; o += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(lds_n + o);  // the same address in every lane
+      count += pair_parts(v.x, cand, cap, capc, rc) + pair_parts(v.y, cand, cap, capc, rc) +
+               pair_parts(v.z, cand, cap, capc, rc) + pair_parts(v.w, cand, cap, capc, rc);
+    }
+    int best = (int64_t)count * H <= a.split_slots ? cand : hi;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) best = min(best, __shfl_xor(best, m));
+    __syncthreads();  // every wave has read lds_red
+    if (lane == 0) lds_red[w] = best;
+  }
+  __syncthreads();
+  const int T = min(min(lds_red[0], lds_red[1]), min(lds_red[2], lds_red[3]));
+  const float rT = 1.0f / (float)T;
+  const int capT = cap * T;
+  // wave 0: lane l takes a run of C pairs, a wave prefix sum gives each run's first part
+  const int u = (int)(blockIdx.x / (unsigned)H);
+  __shared__ SplitItem found;
+  if (w == 0) {
+    const int C = (pairs + 63) / 64;
+    const int o0 = min(pairs, lane * C), o1 = min(pairs, o0 + C);
+    int mine = 0;
+    for (int o = o0; o < o1; ++o) mine += pair_parts(lds_n[o], T, cap, capT, rT);
+    int incl = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    if (lane == 63) found = SplitItem{-1, 0, 0, 0};
+    int pre = incl - mine;
+    if (u >= pre && u < incl) {  // one lane: the run that holds part u
+      for (int o = o0; o < o1; ++o) {
+        const int np = pair_parts(lds_n[o], T, cap, capT, rT);
+        if (u < pre + np) {
+          found = SplitItem{o * H + (int)(blockIdx.x % (unsigned)H), u - pre, np, pre};
+          break;
+        }
+        pre += np;
+      }
+    }
+  }
+  __syncthreads();
+  return found;
+}
+
 template <bool ALIGNED, int D, bool MASKED, bool GEN>
 __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) pa_prefill_mfma(PrefillArgs a) {
   using T = Tile<D>;
@@ -312,6 +454,9 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   __shared__ __attribute__((aligned(1024))) char lds_k1[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v1[T::kBytes];
+  __shared__ __attribute__((aligned(16))) int lds_n[kPrefillSplitTarget];  // split launches: tiles per pair
+  __shared__ int64_t lds_sum[kThreads / 64];
+  __shared__ int lds_red[kThreads / 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -323,13 +468,19 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   // The rows of a work item are (position, query head) pairs of the G query
   // heads that read its kv head, position-major: packed row r is position
   // r / G of head kvh * G + r % G, so every K/V tile serves the whole group
-  // and short queries still fill the waves. Workgroup w runs part
-  // w / num_work of work item w % num_work; consecutive work items of one
-  // (sequence, kv head) are batch * num_kv_heads apart, on one XCD when that
-  // is a multiple of 8.
-  const int n = a.num_work;
-  const int item = (int)(blockIdx.x % (unsigned)n);
-  const int part = (int)(blockIdx.x / (unsigned)n);
+  // and short queries still fill the waves. Unsplit, workgroup w runs work
+  // item w; consecutive work items of one (sequence, kv head) are batch *
+  // num_kv_heads apart, on one XCD when that is a multiple of 8. Split, see
+  // split_assign.
+  int item = (int)blockIdx.x, part = 0, n_parts = 1, u0 = 0;
+  if (a.kv_splits > 1) {
+    const SplitItem si = split_assign(a, lds_n, lds_sum, lds_red);
+    if (si.item < 0) return;  // past the list of parts (uniform across the workgroup)
+    item = si.item;
+    part = si.part;
+    n_parts = si.n_parts;
+    u0 = si.u0;
+  }
   const int G = a.group;
   int task = item;
   const int kvh = task % a.num_kv_heads;
@@ -353,8 +504,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   const int tile_last_pos = (min(q0 + kBM, R) - 1) / G;
   const int kv_end = a.causal ? min(ctx, tile_last_pos + offset + 1) : ctx;
   const int n_tiles_all = (kv_end + kBN - 1) / kBN;
-  // this workgroup's tiles [t_lo, n_tiles)
-  const int n_parts = a.kv_splits;
+  // this workgroup's tiles [t_lo, n_tiles): part `part` of n_parts
   const int t_lo = (int)((int64_t)part * n_tiles_all / n_parts);
   const int n_tiles = (int)((int64_t)(part + 1) * n_tiles_all / n_parts);
 
@@ -629,7 +779,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   // (the reference is wave-uniform per row: m_run of this lane's row; a row
   // that saw no key keeps -inf, sum 0 and a zero output). Device-coherent
   // 16-byte stores: lane (col, half) holds dims 32db + 8g + 4half .. +4.
-  const size_t slot = (size_t)item * a.kv_splits + part;
+  const size_t slot = (size_t)(u0 + part) * a.num_kv_heads + kvh;  // workspace entry of this part
   if (wave_has_rows) {
     const float l_tot = sum_xor32(l_run);
     if (row_abs < R) {
@@ -649,73 +799,117 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   if (tid == 0) lds_last = arrive_last(a.ws_ctr + item, a.epoch, (uint32_t)n_parts);
   __syncthreads();
   if (!lds_last) return;
-  // Merge the parts in order ("Week 2 Day 5", Task 2: common maximum, one
-  // factor per partial, one denominator); rows past L are not stored. A row
-  // without any visible key ends as 0 / 0, as in the unsplit path. Thread t
-  // takes 4 dims of a row, kRowsPerPass rows per pass; the loads of
-  // kMergePasses passes are in flight together.
+  // Merge the parts in order ("Week 2 Day 5", Task 2: rescale each partial
+  // to a common maximum, one denominator), the maximum kept as a running
+  // one: a part that raises it rescales what came before. Rows past L are
+  // not stored; a row without any visible key ends as 0 / 0, as in the
+  // unsplit path. Thread t takes 4 dims of kRowsPerThr rows kRowsPerPass
+  // apart; the loads of kTrip parts for all of them are in flight together
+  // (a missing part re-reads the last one and is not folded in). One part
+  // per trip: the merge is bound by the misses one CU keeps in flight, and
+  // two parts per trip measured no faster.
   constexpr int kThrPerRow = D / 4;
-  constexpr int kRowsPerPass = kThreads / kThrPerRow;
-  constexpr int kMergePasses = 2;
+  constexpr int kRowsPerPass = kThreads / kThrPerRow;  // 16, 8, 4 at D = 64, 128, 256
+  constexpr int kRowsPerThr = 8;
+  constexpr int kTrip = 1;
+  constexpr int kChunks = kBM / (kRowsPerPass * kRowsPerThr);
   const int rows_here = min(kBM, R - q0);
-  const size_t slot0 = (size_t)item * a.kv_splits;
   const int d4 = 4 * (tid % kThrPerRow);
-  for (int r0p = 0; r0p < rows_here; r0p += kRowsPerPass * kMergePasses) {
-    {  // n_parts <= kv_splits <= kPrefillMaxSplits
-      f32x2_t ml[kMergePasses][kPrefillMaxSplits];
-      f32x4_t av[kMergePasses][kPrefillMaxSplits];
+  for (int ch = 0; ch < kChunks; ++ch) {
+    const int rb = ch * kRowsPerPass * kRowsPerThr + tid / kThrPerRow;  // this thread's first row of the chunk
+    if (rb >= rows_here) break;
+    float M[kRowsPerThr], den[kRowsPerThr];
+    f32x4_t num[kRowsPerThr];
 #pragma unroll
-      for (int ps = 0; ps < kMergePasses; ++ps) {
-        const int r = min(r0p + ps * kRowsPerPass + tid / kThrPerRow, rows_here - 1);  // re-read a valid row
+    for (int k = 0; k < kRowsPerThr; ++k) {
+      M[k] = -INFINITY;
+      den[k] = 0.f;
+      num[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int s = 0; s < n_parts; s += kTrip) {
+      f32x2_t ml[kTrip][kRowsPerThr];
+      f32x4_t av[kTrip][kRowsPerThr];
 #pragma unroll
-        for (int s = 0; s < kPrefillMaxSplits; ++s) {
-          const size_t rr = (slot0 + min(s, n_parts - 1)) * kBM + r;
-          ml[ps][s] = load_coherent_x2(a.ws_ml + rr * 2);
-          av[ps][s] = load_coherent_x4(a.ws_acc + rr * D + d4);
+      for (int h = 0; h < kTrip; ++h) {
+        const size_t e = ((size_t)(u0 + min(s + h, n_parts - 1)) * a.num_kv_heads + kvh) * kBM;
+#pragma unroll
+        for (int k = 0; k < kRowsPerThr; ++k) {
+          const int r = min(rb + k * kRowsPerPass, rows_here - 1);  // re-read a valid row
+          ml[h][k] = load_coherent_x2(a.ws_ml + (e + r) * 2);
+          av[h][k] = load_coherent_x4(a.ws_acc + (e + r) * D + d4);
         }
       }
       wait_loads_x(ml, av);
 #pragma unroll
-      for (int ps = 0; ps < kMergePasses; ++ps) {
-        const int r = r0p + ps * kRowsPerPass + tid / kThrPerRow;
-        if (r >= rows_here) continue;
-        float M = -INFINITY;
+      for (int h = 0; h < kTrip; ++h) {
+        if (s + h >= n_parts) break;
 #pragma unroll
-        for (int s = 0; s < kPrefillMaxSplits; ++s)
-          if (s < n_parts) M = fmaxf(M, ml[ps][s].x);
-        float den = 0.f;
-        f32x4_t num = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < kPrefillMaxSplits; ++s) {
-          if (s >= n_parts) continue;
-          const float f = ml[ps][s].x == -INFINITY ? 0.f : fast_exp2(ml[ps][s].x - M);
-          den = fmaf(f, ml[ps][s].y, den);
-          num.x = fmaf(f, av[ps][s].x, num.x);
-          num.y = fmaf(f, av[ps][s].y, num.y);
-          num.z = fmaf(f, av[ps][s].z, num.z);
-          num.w = fmaf(f, av[ps][s].w, num.w);
+        for (int k = 0; k < kRowsPerThr; ++k) {
+          const float m = ml[h][k].x;
+          if (m == -INFINITY) continue;  // a part without a visible key for this row
+          const float Mn = fmaxf(M[k], m);
+          const float fo = fast_exp2(M[k] - Mn);  // 0 while M is -inf
+          const float fn = fast_exp2(m - Mn);
+          den[k] = fmaf(fn, ml[h][k].y, den[k] * fo);
+          num[k].x = fmaf(fn, av[h][k].x, num[k].x * fo);
+          num[k].y = fmaf(fn, av[h][k].y, num[k].y * fo);
+          num[k].z = fmaf(fn, av[h][k].z, num[k].z * fo);
+          num[k].w = fmaf(fn, av[h][k].w, num[k].w * fo);
+          M[k] = Mn;
         }
-        const int pr = q0 + r;  // packed row: position pr / G of head kvh * G + pr % G
-        const int hr = kvh * G + pr % G;
-        const size_t orow =
-            a.qstart ? (size_t)(start + pr / G) * a.num_q_heads + hr : ((size_t)b * a.num_q_heads + hr) * L + pr / G;
-        const u32x2_t w = {pack_bf16x2(num.x / den, num.y / den), pack_bf16x2(num.z / den, num.w / den)};
-        if (!GEN || d4 < a.dv) *reinterpret_cast<u32x2_t*>(a.out + orow * (GEN ? a.dv : D) + d4) = w;
       }
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerThr; ++k) {
+      const int r = rb + k * kRowsPerPass;
+      if (r >= rows_here) continue;
+      const int pr = q0 + r;  // packed row: position pr / G of head kvh * G + pr % G
+      const int hr = kvh * G + pr % G;
+      const size_t orow =
+          a.qstart ? (size_t)(start + pr / G) * a.num_q_heads + hr : ((size_t)b * a.num_q_heads + hr) * L + pr / G;
+      const u32x2_t w = {pack_bf16x2(num[k].x / den[k], num[k].y / den[k]),
+                         pack_bf16x2(num[k].z / den[k], num[k].w / den[k])};
+      if (!GEN || d4 < a.dv) *reinterpret_cast<u32x2_t*>(a.out + orow * (GEN ? a.dv : D) + d4) = w;
     }
   }
 }
 
+// CUs and workgroups of one kernel instance the GPU keeps resident (cached
+// per device).
+struct Residency {
+  int cus, slots;
+};
+
+template <bool ALIGNED, int D, bool MASKED, bool GEN>
+Residency resident_slots() {
+  static Residency cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev].slots > 0) return cache[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)pa_prefill_mfma<ALIGNED, D, MASKED, GEN>, kThreads,
+                                                   0) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  cache[dev] = Residency{cus, cus * per_cu};
+  return cache[dev];
+}
+
+template <bool ALIGNED, int D, bool MASKED, bool GEN>
+hipError_t launch_instance(PrefillArgs a, const Plan& p, hipStream_t stream) {
+  // split: one workgroup per workspace entry, the resident ones used
+  const unsigned grid = (unsigned)(a.kv_splits > 1 ? kPrefillSplitTarget : p.num_work);
+  if (a.kv_splits > 1) a.split_slots = min(kPrefillSplitTarget, resident_slots<ALIGNED, D, MASKED, GEN>().slots);
+  hipLaunchKernelGGL((pa_prefill_mfma<ALIGNED, D, MASKED, GEN>), dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D, bool MASKED>
 hipError_t launch_mask(const PrefillArgs& a, const Plan& p, hipStream_t stream) {
-  const unsigned grid = (unsigned)(p.num_work * a.kv_splits);
   if (a.dv != D)  // a head dim without an instance of its own: the next larger one, masked dims, per-row loader
-    hipLaunchKernelGGL((pa_prefill_mfma<false, D, MASKED, true>), dim3(grid), dim3(kThreads), 0, stream, a);
-  else if (p.aligned)
-    hipLaunchKernelGGL((pa_prefill_mfma<true, D, MASKED, false>), dim3(grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((pa_prefill_mfma<false, D, MASKED, false>), dim3(grid), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+    return launch_instance<false, D, MASKED, true>(a, p, stream);
+  if (p.aligned) return launch_instance<true, D, MASKED, false>(a, p, stream);
+  return launch_instance<false, D, MASKED, false>(a, p, stream);
 }
 
 template <int D>

@@ -74,16 +74,18 @@ int main() {
         CHECK(p.bt_entries == pa::kDecodeWindow / 16 + 2);
       } else {
         CHECK(p.n_qtiles == (G * L + 127) / 128);
-        // 3 * 8 * n_qtiles work items, fewer than 512: the key range (4800
-        // keys) splits into as many parts as keep 512 workgroups busy, at most 4
+        // 3 * 8 * n_qtiles work items, fewer than 512: room for up to 8
+        // parts of each key range (4800 keys, 75 tiles); the kernel picks
+        // each item's count
         const int64_t nw = int64_t(3) * 8 * p.n_qtiles;
         CHECK(p.num_work == nw);
-        const int want = int(std::max<int64_t>(1, std::min<int64_t>(pa::kPrefillMaxSplits, pa::kPrefillSplitTarget / nw)));
-        CHECK(p.kv_splits == want);
+        const int want = pa::kPrefillMaxSplits;
+        CHECK(want == 8 && p.kv_splits == want);
         if (want > 1) {
           CHECK(p.ws_ctr_offset == 0 && p.ws_ml_offset >= size_t(nw) * 8 && p.ws_ml_offset % 256 == 0);
-          CHECK(p.ws_acc_offset >= p.ws_ml_offset + size_t(nw) * want * 128 * 2 * 4 && p.ws_acc_offset % 256 == 0);
-          CHECK(p.workspace_bytes >= p.ws_acc_offset + size_t(nw) * want * 128 * 128 * 4);
+          // one entry per workgroup of the split launch
+          CHECK(p.ws_acc_offset >= p.ws_ml_offset + size_t(512) * 128 * 2 * 4 && p.ws_acc_offset % 256 == 0);
+          CHECK(p.workspace_bytes >= p.ws_acc_offset + size_t(512) * 128 * 128 * 4);
         } else {
           CHECK(p.workspace_bytes == 0);
         }
@@ -97,9 +99,11 @@ int main() {
   CHECK(p.n_qtiles == 3 && p.num_work == 6 && p.kv_splits == 1);  // 192 keys: one part of two tiles at most
   CHECK(pa::make_plan(shape(1, 4, 2, 150, 128, 64, 4), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(p.kv_splits == 2 && p.workspace_bytes > 0);
+  CHECK(pa::make_plan(shape(1, 4, 2, 150, 128, 64, 7), 0, 0, true, &p, &err) == pa::kOk);
+  CHECK(p.kv_splits == 3);  // 448 keys: 7 tiles, three parts of two at most
   CHECK(pa::make_plan(shape(8, 32, 8, 65, 128, 128, 29), 0, 0, true, &p, &err) == pa::kOk);
   // the chunked continuation: 4 x 65 rows per kv head
-  CHECK(p.n_qtiles == 3 && p.num_work == 192 && p.kv_splits == 2);
+  CHECK(p.n_qtiles == 3 && p.num_work == 192 && p.kv_splits == 8);
   CHECK(pa::make_plan(shape(2, 128, 8, 256, 128, 128, 16), 0, 0, true, &p, &err) == pa::kOk);
   CHECK(p.num_work == 512 && p.kv_splits == 1 && p.workspace_bytes == 0);
   // the five measured shapes

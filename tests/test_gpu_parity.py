@@ -424,6 +424,41 @@ def test_prefill_key_range_split(L, ctx, ps, Hq, Hkv, causal):
     assert (ctr == 0).all(), "the last part resets its counter"
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,L,D,seed", [
+    (20, 6, 3, 70, 128, 1),   # 40 (sequence, row tile) pairs, 3 kv heads: list places not a multiple of 8
+    (48, 8, 8, 17, 128, 2),   # 48 one-tile pairs, 8 kv heads: 384 work items, contexts 17 .. 4000
+    (6, 4, 4, 130, 256, 3),   # head dim 256: one resident workgroup per CU
+    (10, 8, 2, 40, 64, 4),    # head dim 64: three resident workgroups per CU
+])
+def test_prefill_split_assignment(B, Hq, Hkv, L, D, seed):
+    """Key-range parts sized to the launch: pairs of very different lengths
+    (one tile to dozens) get from one part to eight, all parts resident at
+    once; every output row is written once and matches the oracle, and the
+    run is bit-reproducible."""
+    import torch
+    from paged_flashattention_kv_amd import native
+
+    rng = np.random.default_rng(seed)
+    ctx = [int(L + x) for x in rng.integers(0, 4000, size=B)]
+    ctx[0] = L  # a pair of one tile
+    p = small(1200 + seed, B=B, Hq=Hq, Hkv=Hkv, L=L, ctx=ctx, ps=64, poison=True, D=D)
+    max_pages = p.block_table.shape[1]
+    need = native.workspace_bytes(B, Hq, Hkv, L, D, 64, max_pages, PREFILL, 0)
+    assert need > 0, "the case must take the split"
+    say(f"split assignment B={B} H={Hq}/{Hkv} L={L} D={D} workspace={need}")
+    want = ref(p)
+    d = to_device(p)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    out = torch.full_like(d["query"], float("nan"))  # a row left unwritten stays NaN
+    native.paged_attention(d["query"], d["key_pages"], d["value_pages"], d["block_table"], d["context_lens"],
+                           p.page_size, p.scale, p.causal, out=out, workspace=ws, schedule=PREFILL)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    parity(got, want, "split assignment")
+    again = _prefill_call(p, d, ws)
+    assert np.array_equal(got, again), "the split run must be bit-reproducible"
+
+
 def test_prefill_split_stale_counters():
     """A workspace left by an interrupted call (counters tagged with another
     call, arbitrary partials) is safe to reuse."""
