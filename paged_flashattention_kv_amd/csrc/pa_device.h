@@ -121,34 +121,25 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// 8- and 16-byte device-coherent stores and loads (the same cache policy as
-// the relaxed agent-scope accesses above). The loads are issued as written
-// and not tracked by the compiler: wait_loads_x waits for them.
+// 8- and 16-byte device-coherent stores (the same cache policy as the
+// relaxed agent-scope accesses above).
 __device__ __forceinline__ void store_coherent_x2(float* p, f32x2_t v) {
   asm volatile("global_store_dwordx2 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ void store_coherent_x4(float* p, f32x4_t v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
+// 8- and 16-byte device-coherent loads as relaxed agent-scope 64-bit atomic
+// loads: the compiler tracks them (it waits before each use), so they stay
+// correct wherever it keeps or spills the registers they fill.
 __device__ __forceinline__ f32x2_t load_coherent_x2(const float* p) {
-  f32x2_t v;
-  asm volatile("global_load_dwordx2 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
-  return v;
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(f32x2_t, v);
 }
 __device__ __forceinline__ f32x4_t load_coherent_x4(const float* p) {
-  f32x4_t v;
-  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-// Waits for every vector memory operation of the wave; the loaded values
-// pass through the statement so that their uses come after the wait.
-template <int P, int S>
-__device__ __forceinline__ void wait_loads_x(f32x2_t (&a)[P][S], f32x4_t (&b)[P][S]) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < P; ++i)
-#pragma unroll
-    for (int j = 0; j < S; ++j) asm volatile("" : "+v"(a[i][j]), "+v"(b[i][j]));
+  const f32x2_t lo = load_coherent_x2(p), hi = load_coherent_x2(p + 2);
+  return f32x4_t{lo.x, lo.y, hi.x, hi.y};
 }
 // Wait until this wave's memory operations (stores included) have completed.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -752,124 +752,101 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   }
   wait_all_loads();  // no load may still be writing this work item's LDS at exit
 
-  // ---- finalize: divide by the row sum, store bf16 ----
-  if (n_parts == 1) {
-    if (!wave_has_rows) return;
-    const float l_tot = sum_xor32(l_run);
-    if (row_abs >= R) return;
-    const float inv = 1.f / l_tot;
-    const size_t orow = a.qstart ? (size_t)(start + pos) * a.num_q_heads + head
-                                 : ((size_t)b * a.num_q_heads + head) * L + pos;
-    uint16_t* op = a.out + orow * (GEN ? a.dv : D);
-#pragma unroll
-    for (int db = 0; db < T::kDb; ++db) {
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int d0 = 32 * db + 8 * grp + 4 * half;
-        if (GEN && d0 >= a.dv) continue;  // a masked dim (dv is a multiple of 8)
-        const u32x2_t w = {pack_bf16x2(acc_o[db][4 * grp] * inv, acc_o[db][4 * grp + 1] * inv),
-                           pack_bf16x2(acc_o[db][4 * grp + 2] * inv, acc_o[db][4 * grp + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(op + d0) = w;
-      }
-    }
-    return;
-  }
-
   // ---- split key range: leave this part's state, the last part merges ----
-  // (the reference is wave-uniform per row: m_run of this lane's row; a row
-  // that saw no key keeps -inf, sum 0 and a zero output). Device-coherent
-  // 16-byte stores: lane (col, half) holds dims 32db + 8g + 4half .. +4.
-  const size_t slot = (size_t)(u0 + part) * a.num_kv_heads + kvh;  // workspace entry of this part
-  if (wave_has_rows) {
-    const float l_tot = sum_xor32(l_run);
-    if (row_abs < R) {
-      const size_t r = slot * kBM + 32 * wave + col;
-      if (half == 0) store_coherent_x2(a.ws_ml + r * 2, f32x2_t{m_run, l_tot});
+  // State of a part in its workspace entry e: (reference max, row sum) of
+  // row r at ws_ml[(e * 128 + r) * 2], the unnormalised output in the
+  // register layout: chunk c = 4db + g (dims 32db + 8g + 4half .. +4) of
+  // wave w's lane l at ws_acc[((e * 4 + w) * kChunks + c) * 256 + 4l], so
+  // that every 16-byte store and load of a wave covers 1 KiB in one piece.
+  // A row that saw no key keeps -inf, sum 0 and a zero output. The last
+  // part to arrive merges the parts in order ("Week 2 Day 5", Task 2:
+  // rescale each partial to the common maximum, one denominator), every
+  // part from the workspace, its own included, so the sum runs in the same
+  // order whichever part arrives last.
+  constexpr int kChunks = T::kDb * 4;
+  float l_fin;
+  if (n_parts > 1) {
+    const int H = a.num_kv_heads;
+    const size_t entry = (size_t)(u0 + part) * H + kvh;
+    if (wave_has_rows) {
+      const float l_tot = sum_xor32(l_run);
+      if (half == 0 && row_abs < R) store_coherent_x2(a.ws_ml + (entry * kBM + 32 * wave + col) * 2, f32x2_t{m_run, l_tot});
+      float* wp = a.ws_acc + (entry * 4 + wave) * kChunks * 256 + 4 * lane;
 #pragma unroll
       for (int db = 0; db < T::kDb; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
-          store_coherent_x4(a.ws_acc + r * D + 32 * db + 8 * g4 + 4 * half,
-                            f32x4_t{acc_o[db][4 * g4], acc_o[db][4 * g4 + 1], acc_o[db][4 * g4 + 2], acc_o[db][4 * g4 + 3]});
+          store_coherent_x4(wp + (4 * db + g4) * 256, f32x4_t{acc_o[db][4 * g4], acc_o[db][4 * g4 + 1],
+                                                             acc_o[db][4 * g4 + 2], acc_o[db][4 * g4 + 3]});
     }
+    wait_stores();
+    __shared__ bool lds_last;
+    __syncthreads();
+    if (tid == 0) lds_last = arrive_last(a.ws_ctr + item, a.epoch, (uint32_t)n_parts);
+    __syncthreads();
+    if (!lds_last || !wave_has_rows) return;
+    // every part's (max, sum) of this lane's row (rows past R: unused values)
+    f32x2_t ml[kPrefillMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kPrefillMaxSplits; ++s) {
+      const size_t e = (size_t)(u0 + min(s, n_parts - 1)) * H + kvh;
+      ml[s] = load_coherent_x2(a.ws_ml + (e * kBM + 32 * wave + col) * 2);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kPrefillMaxSplits; ++s)
+      if (s < n_parts) M = fmaxf(M, ml[s].x);
+    float den = 0.f;
+#pragma unroll
+    for (int db = 0; db < T::kDb; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;
+    for (int s = 0; s < n_parts; ++s) {
+      const size_t e = (size_t)(u0 + s) * H + kvh;
+      const float* rp = a.ws_acc + (e * 4 + wave) * kChunks * 256 + 4 * lane;
+      f32x4_t av[kChunks];
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) av[c] = load_coherent_x4(rp + c * 256);
+      float ms = ml[0].x, ls = ml[0].y;
+#pragma unroll
+      for (int k = 1; k < kPrefillMaxSplits; ++k)
+        if (s == k) {
+          ms = ml[k].x;
+          ls = ml[k].y;
+        }
+      const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - M);  // a part without a visible key adds nothing
+      den = fmaf(f, ls, den);
+#pragma unroll
+      for (int db = 0; db < T::kDb; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          acc_o[db][4 * g4] = fmaf(f, av[4 * db + g4].x, acc_o[db][4 * g4]);
+          acc_o[db][4 * g4 + 1] = fmaf(f, av[4 * db + g4].y, acc_o[db][4 * g4 + 1]);
+          acc_o[db][4 * g4 + 2] = fmaf(f, av[4 * db + g4].z, acc_o[db][4 * g4 + 2]);
+          acc_o[db][4 * g4 + 3] = fmaf(f, av[4 * db + g4].w, acc_o[db][4 * g4 + 3]);
+        }
+    }
+    l_fin = den;
+  } else {
+    if (!wave_has_rows) return;
+    l_fin = sum_xor32(l_run);
   }
-  wait_stores();
-  __shared__ bool lds_last;
-  __syncthreads();
-  if (tid == 0) lds_last = arrive_last(a.ws_ctr + item, a.epoch, (uint32_t)n_parts);
-  __syncthreads();
-  if (!lds_last) return;
-  // Merge the parts in order ("Week 2 Day 5", Task 2: rescale each partial
-  // to a common maximum, one denominator), the maximum kept as a running
-  // one: a part that raises it rescales what came before. Rows past L are
-  // not stored; a row without any visible key ends as 0 / 0, as in the
-  // unsplit path. Thread t takes 4 dims of kRowsPerThr rows kRowsPerPass
-  // apart; the loads of kTrip parts for all of them are in flight together
-  // (a missing part re-reads the last one and is not folded in). One part
-  // per trip: the merge is bound by the misses one CU keeps in flight, and
-  // two parts per trip measured no faster.
-  constexpr int kThrPerRow = D / 4;
-  constexpr int kRowsPerPass = kThreads / kThrPerRow;  // 16, 8, 4 at D = 64, 128, 256
-  constexpr int kRowsPerThr = 8;
-  constexpr int kTrip = 1;
-  constexpr int kChunks = kBM / (kRowsPerPass * kRowsPerThr);
-  const int rows_here = min(kBM, R - q0);
-  const int d4 = 4 * (tid % kThrPerRow);
-  for (int ch = 0; ch < kChunks; ++ch) {
-    const int rb = ch * kRowsPerPass * kRowsPerThr + tid / kThrPerRow;  // this thread's first row of the chunk
-    if (rb >= rows_here) break;
-    float M[kRowsPerThr], den[kRowsPerThr];
-    f32x4_t num[kRowsPerThr];
+
+  // ---- finalize: divide by the row sum, store bf16 ----
+  if (row_abs >= R) return;
+  const float inv = 1.f / l_fin;  // a row without any visible key: 0 / 0
+  const size_t orow = a.qstart ? (size_t)(start + pos) * a.num_q_heads + head
+                               : ((size_t)b * a.num_q_heads + head) * L + pos;
+  uint16_t* op = a.out + orow * (GEN ? a.dv : D);
 #pragma unroll
-    for (int k = 0; k < kRowsPerThr; ++k) {
-      M[k] = -INFINITY;
-      den[k] = 0.f;
-      num[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int s = 0; s < n_parts; s += kTrip) {
-      f32x2_t ml[kTrip][kRowsPerThr];
-      f32x4_t av[kTrip][kRowsPerThr];
+  for (int db = 0; db < T::kDb; ++db) {
 #pragma unroll
-      for (int h = 0; h < kTrip; ++h) {
-        const size_t e = ((size_t)(u0 + min(s + h, n_parts - 1)) * a.num_kv_heads + kvh) * kBM;
-#pragma unroll
-        for (int k = 0; k < kRowsPerThr; ++k) {
-          const int r = min(rb + k * kRowsPerPass, rows_here - 1);  // re-read a valid row
-          ml[h][k] = load_coherent_x2(a.ws_ml + (e + r) * 2);
-          av[h][k] = load_coherent_x4(a.ws_acc + (e + r) * D + d4);
-        }
-      }
-      wait_loads_x(ml, av);
-#pragma unroll
-      for (int h = 0; h < kTrip; ++h) {
-        if (s + h >= n_parts) break;
-#pragma unroll
-        for (int k = 0; k < kRowsPerThr; ++k) {
-          const float m = ml[h][k].x;
-          if (m == -INFINITY) continue;  // a part without a visible key for this row
-          const float Mn = fmaxf(M[k], m);
-          const float fo = fast_exp2(M[k] - Mn);  // 0 while M is -inf
-          const float fn = fast_exp2(m - Mn);
-          den[k] = fmaf(fn, ml[h][k].y, den[k] * fo);
-          num[k].x = fmaf(fn, av[h][k].x, num[k].x * fo);
-          num[k].y = fmaf(fn, av[h][k].y, num[k].y * fo);
-          num[k].z = fmaf(fn, av[h][k].z, num[k].z * fo);
-          num[k].w = fmaf(fn, av[h][k].w, num[k].w * fo);
-          M[k] = Mn;
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kRowsPerThr; ++k) {
-      const int r = rb + k * kRowsPerPass;
-      if (r >= rows_here) continue;
-      const int pr = q0 + r;  // packed row: position pr / G of head kvh * G + pr % G
-      const int hr = kvh * G + pr % G;
-      const size_t orow =
-          a.qstart ? (size_t)(start + pr / G) * a.num_q_heads + hr : ((size_t)b * a.num_q_heads + hr) * L + pr / G;
-      const u32x2_t w = {pack_bf16x2(num[k].x / den[k], num[k].y / den[k]),
-                         pack_bf16x2(num[k].z / den[k], num[k].w / den[k])};
-      if (!GEN || d4 < a.dv) *reinterpret_cast<u32x2_t*>(a.out + orow * (GEN ? a.dv : D) + d4) = w;
+    for (int grp = 0; grp < 4; ++grp) {
+      const int d0 = 32 * db + 8 * grp + 4 * half;
+      if (GEN && d0 >= a.dv) continue;  // a masked dim (dv is a multiple of 8)
+      const u32x2_t w = {pack_bf16x2(acc_o[db][4 * grp] * inv, acc_o[db][4 * grp + 1] * inv),
+                         pack_bf16x2(acc_o[db][4 * grp + 2] * inv, acc_o[db][4 * grp + 3] * inv)};
+      *reinterpret_cast<u32x2_t*>(op + d0) = w;
     }
   }
 }
