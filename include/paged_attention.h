@@ -125,11 +125,15 @@ int paged_attention(const void* query, const void* key_pages, const void* value_
  * one input, "Week 3 Day 5", Task 3, and for tuning sweeps).
  *   schedule           PA_SCHEDULE_AUTO / _DECODE / _PREFILL. DECODE needs
  *                      query_len * num_q_heads / num_kv_heads <= 8.
- *   decode_work_items  the decode schedule splits the total K/V work (sum of
+ *   decode_work_items  the decode schedule cuts the total K/V work (sum of
  *                      context lengths times kv heads, in 64-key granules)
- *                      evenly over this many work items; 0 = as many as the
- *                      GPU keeps resident at once (at most 2048); otherwise
- *                      1 .. 65536. Ignored by the prefill schedule.
+ *                      into contiguous ranges over this many work items,
+ *                      sized by a cost model (a segment start costs extra;
+ *                      with two resident per CU, the grid's second half
+ *                      takes 12/16 of a first-half share); 0 = as many as
+ *                      the GPU keeps resident at once (at most 2048);
+ *                      otherwise 1 .. 65536. Ignored by the prefill
+ *                      schedule.
  * Same arguments, preconditions and errors as paged_attention otherwise.
  */
 int paged_attention_ex(const void* query, const void* key_pages, const void* value_pages,

@@ -16,8 +16,9 @@
 //   the G query heads that read the kv head, position-major (row r:
 //   position r / G of head kvh * G + r % G), so each K/V tile serves the
 //   whole group and a short query still fills the waves. K/V tiles are 64
-//   keys. A launch with few work items splits each key range into up to four
-//   parts run by separate workgroups, merged by the one that arrives last.
+//   keys. A launch with few work items splits the key ranges into parts
+//   sized from its own context lengths (up to eight per work item, all of
+//   them resident at once), merged by the part that arrives last.
 //   Matrix core: v_mfma_f32_32x32x16_bf16 (fp32 accumulate). Scores are
 //   computed transposed, S^T = K Q^T (A = K rows from LDS, B = the wave's
 //   Q^T held in registers for the whole loop), so lane l holds 16 scores of
@@ -53,8 +54,9 @@
 // t is computed, one barrier per tile.
 //
 // Work items are ordered so that the heaviest causal row tiles start first;
-// the row tiles of one (sequence, kv head) are batch * num_kv_heads apart,
-// on one XCD (shared L2) when that is a multiple of 8.
+// unsplit, the row tiles of one (sequence, kv head) are batch * num_kv_heads
+// apart, on one XCD (shared L2) when that is a multiple of 8; split, all
+// parts of one kv head run on one XCD when there are 8 kv heads.
 
 #include "pa_device.h"
 #include "pa_kernels.h"
