@@ -762,9 +762,10 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   // that every 16-byte store and load of a wave covers 1 KiB in one piece.
   // A row that saw no key keeps -inf, sum 0 and a zero output. The last
   // part to arrive merges the parts in order ("Week 2 Day 5", Task 2:
-  // rescale each partial to the common maximum, one denominator), every
-  // part from the workspace, its own included, so the sum runs in the same
-  // order whichever part arrives last.
+  // rescale each partial to the common maximum, one denominator): the
+  // others from the workspace, its own from its registers (the values it
+  // stored), so the sum runs in the same order, over the same values,
+  // whichever part arrives last.
   constexpr int kChunks = T::kDb * 4;
   float l_fin;
   if (n_parts > 1) {
@@ -799,16 +800,25 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
     for (int s = 0; s < kPrefillMaxSplits; ++s)
       if (s < n_parts) M = fmaxf(M, ml[s].x);
     float den = 0.f;
+    f32x16_t mo[T::kDb];  // the merged output (acc_o still holds this part's)
 #pragma unroll
     for (int db = 0; db < T::kDb; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;
+      for (int i = 0; i < 16; ++i) mo[db][i] = 0.f;
     for (int s = 0; s < n_parts; ++s) {
-      const size_t e = (size_t)(u0 + s) * H + kvh;
-      const float* rp = a.ws_acc + (e * 4 + wave) * kChunks * 256 + 4 * lane;
       f32x4_t av[kChunks];
+      if (s != part) {
+        const size_t e = (size_t)(u0 + s) * H + kvh;
+        const float* rp = a.ws_acc + (e * 4 + wave) * kChunks * 256 + 4 * lane;
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) av[c] = load_coherent_x4(rp + c * 256);
+        for (int c = 0; c < kChunks; ++c) av[c] = load_coherent_x4(rp + c * 256);
+      } else {
+#pragma unroll
+        for (int db = 0; db < T::kDb; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            av[4 * db + g4] = f32x4_t{acc_o[db][4 * g4], acc_o[db][4 * g4 + 1], acc_o[db][4 * g4 + 2], acc_o[db][4 * g4 + 3]};
+      }
       float ms = ml[0].x, ls = ml[0].y;
 #pragma unroll
       for (int k = 1; k < kPrefillMaxSplits; ++k)
@@ -822,12 +832,14 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
       for (int db = 0; db < T::kDb; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          acc_o[db][4 * g4] = fmaf(f, av[4 * db + g4].x, acc_o[db][4 * g4]);
-          acc_o[db][4 * g4 + 1] = fmaf(f, av[4 * db + g4].y, acc_o[db][4 * g4 + 1]);
-          acc_o[db][4 * g4 + 2] = fmaf(f, av[4 * db + g4].z, acc_o[db][4 * g4 + 2]);
-          acc_o[db][4 * g4 + 3] = fmaf(f, av[4 * db + g4].w, acc_o[db][4 * g4 + 3]);
+          mo[db][4 * g4] = fmaf(f, av[4 * db + g4].x, mo[db][4 * g4]);
+          mo[db][4 * g4 + 1] = fmaf(f, av[4 * db + g4].y, mo[db][4 * g4 + 1]);
+          mo[db][4 * g4 + 2] = fmaf(f, av[4 * db + g4].z, mo[db][4 * g4 + 2]);
+          mo[db][4 * g4 + 3] = fmaf(f, av[4 * db + g4].w, mo[db][4 * g4 + 3]);
         }
     }
+#pragma unroll
+    for (int db = 0; db < T::kDb; ++db) acc_o[db] = mo[db];
     l_fin = den;
   } else {
     if (!wave_has_rows) return;
