@@ -77,11 +77,12 @@ PROBLEMS = {
     "mixed_batch": ("varlen", "mixed_batch"),
 }
 EXTRA_CASES = [
-    "long_prefill", "chunked_continuation", "long_decode", "kv_append_prefill", "kv_append_decode",
-    "masked_decode", "masked_prefill", "mixed_batch",
+    "long_prefill", "long_prefill_64x32", "chunked_continuation", "long_decode", "kv_append_prefill",
+    "kv_append_decode", "masked_decode", "masked_prefill", "mixed_batch",
 ]
 CASE_PROBLEM = {
-    "decode_batch": "decode_batch", "long_prefill": "long_prefill", "chunked_continuation": "chunked_continuation",
+    "decode_batch": "decode_batch", "long_prefill": "long_prefill", "long_prefill_64x32": "long_prefill",
+    "chunked_continuation": "chunked_continuation",
     "long_decode": "long_decode", "kv_append_prefill": "long_prefill", "kv_append_decode": "decode_batch",
     "masked_decode": "decode_batch", "masked_prefill": "long_prefill", "mixed_batch": "mixed_batch",
 }
@@ -167,11 +168,12 @@ def _bf(a, dev="cuda:0"):
 class Case:
     """Device copies of a problem plus a callable that runs one step."""
 
-    def __init__(self, p, copies: int):
+    def __init__(self, p, copies: int, schedule: int = 0):
         import torch
         from paged_flashattention_kv_amd import native
 
         self.p = p
+        self.schedule = schedule
         dev = "cuda:0"
         self.q = _bf(p.query)
         k = _bf(p.key_pages)
@@ -181,7 +183,7 @@ class Case:
         self.ctx = torch.from_numpy(p.context_lens.copy()).to(dev)
         self.out = torch.empty_like(self.q)
         need = native.workspace_bytes(p.batch, p.num_q_heads, p.num_kv_heads, p.query_len, p.head_dim,
-                                      p.page_size, p.max_pages)
+                                      p.page_size, p.max_pages, schedule, 0)
         self.ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
         self.i = 0
         self._native = native
@@ -190,7 +192,7 @@ class Case:
         k, v = self.pools[self.i % len(self.pools)]
         self.i += 1
         self._native.paged_attention(self.q, k, v, self.bt, self.ctx, self.p.page_size, self.p.scale, self.p.causal,
-                                     out=self.out, workspace=self.ws)
+                                     out=self.out, workspace=self.ws, schedule=self.schedule)
 
     def time(self, steps: int, warmup: int):
         """ms per step over exactly ``steps`` calls, HIP events on the launch stream.
@@ -338,6 +340,10 @@ def time_case(name: str, probs: dict, steps: int, warmup: int) -> dict:
             info["mask_bytes"] = c.mask_bytes
     elif name in ("long_prefill", "long_decode"):
         c = Case(p, 1)  # long_decode: 2 GiB per step already exceeds the Infinity Cache
+    elif name == "long_prefill_64x32":
+        from paged_flashattention_kv_amd import native
+
+        c = Case(p, 1, schedule=native.SCHEDULE_PREFILL_64X32)
     elif name == "kv_append_prefill":
         c = AppendCase(p, 2048, 8)
         info["bytes"] = c.bytes
@@ -437,6 +443,12 @@ def describe_extra(name: str, p, st: dict, info: dict) -> dict:
         return {"workload": "B=4 L=ctx=2048 H_q=32 H_kv=8 D=128 causal, page_size=128 shuffled", **timing,
                 "value": round(tf, 2), "unit": "TFLOP/s",
                 "roofline": _mfma_roofline(p.flops(), ms, "pa_prefill_mfma", "long_prefill")}
+    if name == "long_prefill_64x32":
+        tf = p.flops() / (ms * 1e-3) / 1e12
+        return {"workload": "long_prefill at the stated tiling: 64 packed query rows x 32 keys per tile "
+                            "(PA_SCHEDULE_PREFILL_64X32; the row above is the automatic 128 x 64 tiling)",
+                **timing, "value": round(tf, 2), "unit": "TFLOP/s",
+                "roofline": _mfma_roofline(p.flops(), ms, "pa_prefill_mfma (64x32)", "", traffic=False)}
     if name == "chunked_continuation":
         return {"workload": "B=8 L=65 history U[1000,3600] (seed 4) H_q=32 H_kv=8 D=128 causal, page_size=128",
                 **timing, "tflops": round(p.flops() / (ms * 1e-3) / 1e12, 2),

@@ -64,7 +64,15 @@ enum {
 enum {
   PA_SCHEDULE_AUTO = 0,
   PA_SCHEDULE_DECODE = 1,  /* short-query schedule, context split over work items */
-  PA_SCHEDULE_PREFILL = 2  /* long-query MFMA tiled schedule */
+  PA_SCHEDULE_PREFILL = 2, /* long-query MFMA tiled schedule: 128 packed query
+                              rows x 64 keys per tile */
+  PA_SCHEDULE_PREFILL_64X32 = 3 /* the same schedule at 64 packed query rows x
+                              32 keys per tile, the tiling of the matrix kernel
+                              in "Week 3 Day 5: Paged FlashAttention", Task 1,
+                              for measurements against PREFILL (slower on
+                              MI355X). Explicit only: head dims 64, 128 and
+                              256, no explicit mask (PA_ERR_UNSUPPORTED
+                              otherwise), never split, no workspace */
 };
 
 /*
@@ -123,7 +131,8 @@ int paged_attention(const void* query, const void* key_pages, const void* value_
  * paged_attention_ex -- paged_attention with the schedule and the number of
  * decode work items chosen by the caller (for tests of both schedules on
  * one input, "Week 3 Day 5", Task 3, and for tuning sweeps).
- *   schedule           PA_SCHEDULE_AUTO / _DECODE / _PREFILL. DECODE needs
+ *   schedule           PA_SCHEDULE_AUTO / _DECODE / _PREFILL /
+ *                      _PREFILL_64X32. DECODE needs
  *                      query_len * num_q_heads / num_kv_heads <= 8.
  *   decode_work_items  the decode schedule cuts the total K/V work (sum of
  *                      context lengths times kv heads, in 64-key granules)

@@ -21,6 +21,7 @@ from .native import (  # noqa: F401
     SCHEDULE_AUTO,
     SCHEDULE_DECODE,
     SCHEDULE_PREFILL,
+    SCHEDULE_PREFILL_64X32,
     PagedAttentionError,
     check_metadata,
     check_varlen_metadata,

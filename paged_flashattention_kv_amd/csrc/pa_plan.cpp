@@ -42,7 +42,9 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
     return fail(err, kErrInvalid, "causal attention needs max_pages * page_size >= query_len");
   if (s.batch * s.num_q_heads * s.query_len > INT32_MAX)
     return fail(err, kErrUnsupported, "batch * num_q_heads * query_len exceeds int32");
-  if (schedule < 0 || schedule > 2) return fail(err, kErrInvalid, "schedule must be 0, 1 or 2");
+  if (schedule < 0 || schedule > 3) return fail(err, kErrInvalid, "schedule must be 0, 1, 2 or 3");
+  if (schedule == kSchedulePrefill64x32 && instance_dim(s.head_dim) != s.head_dim)
+    return fail(err, kErrUnsupported, "the 64 x 32 prefill tiling serves head dims 64, 128 and 256");
 
   Plan p;
   p.group = int(s.num_q_heads / s.num_kv_heads);
@@ -75,6 +77,11 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
     p.ws_ml_offset = align_up(size_t(s.batch) * size_t(s.num_kv_heads) * sizeof(uint64_t), 256);
     p.ws_acc_offset = align_up(p.ws_ml_offset + slots * 2 * sizeof(float), 256);
     p.workspace_bytes = align_up(p.ws_acc_offset + slots * size_t(instance_dim(s.head_dim)) * sizeof(float), 256);
+  } else if (schedule == kSchedulePrefill64x32) {
+    p.n_qtiles = int(cdiv(rows, kPrefill64x32Rows));
+    p.aligned = s.page_size % kPrefill64x32Keys == 0;
+    p.num_work = int64_t(p.n_qtiles) * s.num_kv_heads * s.batch;
+    if (p.num_work > INT32_MAX) return fail(err, kErrUnsupported, "prefill grid too large");
   } else {
     // rows of a work item: (position, query head) pairs of one kv head's group
     p.n_qtiles = int(cdiv(rows, kPrefillBlockM));

@@ -43,6 +43,14 @@ constexpr int kPrefillSplitTarget = 512;
 constexpr int kPrefillMaxSplits = 8;
 constexpr int kScheduleDecode = 1;
 constexpr int kSchedulePrefill = 2;
+// The prefill schedule at 64 packed rows x 32 keys per tile (two waves per
+// work item): the tiling of the matrix kernel in "Week 3 Day 5: Paged
+// FlashAttention", Task 1, kept to measure the 128 x 64 tiling against.
+// Explicit only; native head dims (64, 128, 256), no explicit mask, never
+// split.
+constexpr int kSchedulePrefill64x32 = 3;
+constexpr int kPrefill64x32Rows = 64;
+constexpr int kPrefill64x32Keys = 32;
 
 struct Shape {
   int64_t batch = 0, num_q_heads = 0, num_kv_heads = 0, query_len = 0, head_dim = 0;
@@ -59,7 +67,7 @@ struct Plan {
   int work_items = 0;      // decode: requested work items (0 = as many as stay resident)
   int work_cap = 0;        // decode: most work items the workspace is sized for
   int bt_entries = 0;      // decode: block-table entries staged per window
-  int n_qtiles = 0;        // prefill: 128-row tiles of the group * query_len rows of a (sequence, kv head)
+  int n_qtiles = 0;        // prefill: 128-row (64-row) tiles of the group * query_len rows of a (sequence, kv head)
   int kv_splits = 1;       // prefill: parts of each work item's key range (1: no split)
   int ps_log2 = -1;        // log2(page_size) or -1 if not a power of two
   bool aligned = false;    // every tile lies inside one page
@@ -119,9 +127,10 @@ inline ScaleFold fold_scale(float scale) {
   return f;
 }
 
-// Validates `s` and fills `plan`. `schedule` is 0 (auto), 1 (decode) or
-// 2 (prefill); `decode_work_items` is 0 (auto) or an explicit number of
-// decode work items. Returns kOk or a negative code with a message in `err`.
+// Validates `s` and fills `plan`. `schedule` is 0 (auto), 1 (decode), 2
+// (prefill) or 3 (prefill at 64 x 32 tiles); `decode_work_items` is 0 (auto)
+// or an explicit number of decode work items. Returns kOk or a negative code
+// with a message in `err`.
 int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_pool, Plan* plan,
               std::string* err);
 

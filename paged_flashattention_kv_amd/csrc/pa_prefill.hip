@@ -73,16 +73,25 @@ constexpr int kBN = kPrefillBlockN;       // 64 keys
 // chunks of 16 bytes; one global_load_lds instruction (64 lanes x 16 bytes)
 // moves 1024 / (2D) rows, and a wave stages its 16 rows of a tile in D/32
 // instructions.
-template <int D>
+template <int D, int BN = kBN>
 struct Tile {
   static_assert(D == 64 || D == 128 || D == 256, "head dims 64, 128 and 256");
-  static constexpr int kBytes = kBN * 2 * D;  // one K (or V) tile in LDS
+  static constexpr int kBytes = BN * 2 * D;  // one K (or V) tile of BN keys in LDS
   static constexpr int kChunks = D / 8;       // 16-byte chunks per key row
   static constexpr int kRowsPerInst = 512 / D;
   static constexpr int kInsts = D / 32;       // load instructions per wave per tile
   static constexpr int kKs = D / 16;          // 16-dim contraction steps of S = Q K^T
   static constexpr int kDb = D / 32;          // 32-dim output blocks of O = P V
   static constexpr int kBlocksPerCU = D <= 128 ? 2 : 1;  // LDS: 4 tiles per work item
+};
+// A wave's share of the tile loads in a work item of NW waves and BN-key
+// tiles: keys [kKeys w, kKeys (w + 1)) of every tile (16 in both instances),
+// kInsts instructions for K (and as many for V).
+template <int D, int NW, int BN>
+struct Stage {
+  static constexpr int kKeys = BN / NW;
+  static constexpr int kInsts = kKeys / Tile<D>::kRowsPerInst;
+  static_assert(kInsts >= 1, "a wave loads whole instructions");
 };
 // The exponent reference of a row moves only when a tile maximum exceeds it
 // by more than kTau (log2 units), so weights stay <= 2^kTau.
@@ -170,18 +179,19 @@ __device__ __forceinline__ int tile_off(int key, int chunk) { return key * (2 * 
 // Page lookup for the next tile to stage: the element offset of the key row
 // each of the lane's 4 load instructions reads (generic path), or the
 // tile's base row (aligned path, one entry).
-template <bool ALIGNED, int D>
+template <bool ALIGNED, int D, int NW, int BN>
 struct TilePages {
-  size_t row[ALIGNED ? 1 : Tile<D>::kInsts];
+  size_t row[ALIGNED ? 1 : Stage<D, NW, BN>::kInsts];
 };
 
 typedef __attribute__((address_space(4))) const int32_t constant_i32;
 
-template <bool ALIGNED, int D, bool GEN>
+template <bool ALIGNED, int D, bool GEN, int NW, int BN>
 __device__ __forceinline__ void lookup_tile(const PrefillArgs& a, const int32_t* bt_row, size_t page_stride,
                                             size_t head_off, int ctx, int t0, int wave, int lane,
-                                            TilePages<ALIGNED, D>& tp) {
+                                            TilePages<ALIGNED, D, NW, BN>& tp) {
   using T = Tile<D>;
+  using S = Stage<D, NW, BN>;
   if (ALIGNED) {
     // one uniform entry per tile: a scalar load (the table is read-only here)
     const int lp = div_ps(t0, a.page_size, a.ps_log2);
@@ -189,8 +199,8 @@ __device__ __forceinline__ void lookup_tile(const PrefillArgs& a, const int32_t*
     tp.row[0] = (size_t)page * page_stride + head_off + (size_t)(t0 - lp * a.page_size) * (GEN ? a.dv : D);
   } else {
 #pragma unroll
-    for (int i = 0; i < T::kInsts; ++i) {
-      int key = t0 + 16 * wave + T::kRowsPerInst * i + lane / T::kChunks;
+    for (int i = 0; i < S::kInsts; ++i) {
+      int key = t0 + S::kKeys * wave + T::kRowsPerInst * i + lane / T::kChunks;
       key = key < ctx ? key : ctx - 1;  // past the context: re-read a valid row
       const int lp = div_ps(key, a.page_size, a.ps_log2);
       tp.row[i] = (size_t)bt_row[lp] * page_stride + head_off + (size_t)(key - lp * a.page_size) * (GEN ? a.dv : D);
@@ -199,34 +209,36 @@ __device__ __forceinline__ void lookup_tile(const PrefillArgs& a, const int32_t*
 }
 
 // Issues the direct HBM -> LDS loads of one K/V tile. Wave w moves keys
-// [16w, 16w + 16) of the tile: instruction i covers the kRowsPerInst keys
-// from 16w + kRowsPerInst*i; lane l takes key 16w + kRowsPerInst*i + l/kChunks
-// and LDS chunk position l % kChunks, which holds global chunk
+// [16w, 16w + 16) of the tile (kKeys = 16 in both instances): instruction i
+// covers the kRowsPerInst keys from 16w + kRowsPerInst*i; lane l takes key
+// 16w + kRowsPerInst*i + l/kChunks and LDS chunk position l % kChunks, which
+// holds global chunk
 // (l % kChunks) ^ swz(key). A whole aligned tile is one contiguous span of
 // one page: a wave-uniform base (scalar registers) plus a per-lane byte
 // offset that is the same for every tile, so its loads cost no vector
 // arithmetic.
-template <bool ALIGNED, int D, bool GEN>
-__device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages<ALIGNED, D>& tp, int ctx, int t0,
-                                           int wave, int lane, char* kbuf, char* vbuf) {
+template <bool ALIGNED, int D, bool GEN, int NW, int BN>
+__device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages<ALIGNED, D, NW, BN>& tp, int ctx,
+                                           int t0, int wave, int lane, char* kbuf, char* vbuf) {
   using T = Tile<D>;
-  if (ALIGNED && t0 + kBN <= ctx) {
+  using S = Stage<D, NW, BN>;
+  if (ALIGNED && t0 + BN <= ctx) {
     const char* kbase = reinterpret_cast<const char*>(a.kpages + tp.row[0]);
     const char* vbase = reinterpret_cast<const char*>(a.vpages + tp.row[0]);
 #pragma unroll
-    for (int i = 0; i < T::kInsts; ++i) {
-      const int key = 16 * wave + T::kRowsPerInst * i + lane / T::kChunks;  // key inside the tile
+    for (int i = 0; i < S::kInsts; ++i) {
+      const int key = S::kKeys * wave + T::kRowsPerInst * i + lane / T::kChunks;  // key inside the tile
       const int chunk = src_chunk<GEN>(a, (lane % T::kChunks) ^ swz<D>(key));
       const uint32_t off = (uint32_t)(key * (GEN ? a.dv : D) + chunk * 8) * 2u;  // bytes from the tile's first row
-      const int lds_off = wave * 32 * D + i * 1024;
+      const int lds_off = wave * S::kKeys * 2 * D + i * 1024;
       __builtin_amdgcn_global_load_lds((global_void*)(kbase + off), (lds_void*)(kbuf + lds_off), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((global_void*)(vbase + off), (lds_void*)(vbuf + lds_off), 16, 0, 0);
     }
     return;
   }
 #pragma unroll
-  for (int i = 0; i < T::kInsts; ++i) {
-    const int key = 16 * wave + T::kRowsPerInst * i + lane / T::kChunks;  // key inside the tile
+  for (int i = 0; i < S::kInsts; ++i) {
+    const int key = S::kKeys * wave + T::kRowsPerInst * i + lane / T::kChunks;  // key inside the tile
     const int chunk = src_chunk<GEN>(a, (lane % T::kChunks) ^ swz<D>(key));
     size_t row;
     if (ALIGNED) {
@@ -236,7 +248,7 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages
       row = tp.row[i];
     }
     const size_t off = row + (size_t)chunk * 8;
-    const int lds_off = wave * 32 * D + i * 1024;
+    const int lds_off = wave * S::kKeys * 2 * D + i * 1024;
     __builtin_amdgcn_global_load_lds((global_void*)(a.kpages + off), (lds_void*)(kbuf + lds_off), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((global_void*)(a.vpages + off), (lds_void*)(vbuf + lds_off), 16, 0, 0);
   }
@@ -312,11 +324,12 @@ __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt
 
 // Key tiles a work item of row tile `rtile` of a sequence with L query rows
 // and context ctx streams (the whole-tile causal skip included).
+template <int BM, int BN>
 __device__ __forceinline__ int item_tiles(const PrefillArgs& a, int rtile, int L, int ctx) {
   const int R = a.group * L;
-  const int tile_last_pos = (min(rtile * kBM + kBM, R) - 1) / a.group;
+  const int tile_last_pos = (min(rtile * BM + BM, R) - 1) / a.group;
   const int kv_end = a.causal ? min(ctx, tile_last_pos + ctx - L + 1) : ctx;
-  return (kv_end + kBN - 1) / kBN;
+  return (kv_end + BN - 1) / BN;
 }
 
 // What a workgroup of a split launch runs: part `part` of the n_parts of
@@ -347,7 +360,7 @@ __device__ __forceinline__ int pair_parts(int nt, int T, int cap, int capT, floa
 // smallest for which
 //   H_kv * sum_o parts(n_o, T) <= a.split_slots,
 //   parts(n, T) = clamp(ceil(n / T), 1, min(kv_splits, n / 2)),
-// searched over 256 candidates in parallel (one per thread) from
+// searched over NT candidates in parallel (one per thread) from
 // ceil(total / slots) to the longest pair (where every pair has one part),
 // so that every part is resident at once and the longest sequences do not
 // set the time. The parts are listed pair by pair, each once per kv head:
@@ -355,13 +368,14 @@ __device__ __forceinline__ int pair_parts(int nt, int T, int cap, int capT, floa
 // (with 8 kv heads every part of a kv head lands on one XCD and shares its
 // L2); workgroups past the list run nothing. Called by every thread
 // (barriers inside); there are fewer pairs than kPrefillSplitTarget.
+template <int NT, int BM, int BN>
 __device__ SplitItem split_assign(const PrefillArgs& a, int* lds_n, int64_t* lds_sum, int* lds_red) {
   const int nq = a.n_qtiles;
   const int pairs = a.batch * nq;
   const int pairs4 = (pairs + 3) & ~3;  // padded with empty pairs for 4-wide reads
   int64_t sum = 0;
   int longest = 0;
-  for (int o = threadIdx.x; o < pairs4; o += kThreads) {
+  for (int o = threadIdx.x; o < pairs4; o += NT) {
     int t = -1;  // no rows: no part
     if (o < pairs) {
       const int b = o % a.batch, r = nq - 1 - o / a.batch;
@@ -373,7 +387,7 @@ __device__ SplitItem split_assign(const PrefillArgs& a, int* lds_n, int64_t* lds
         live = !(s0 < 0 || s1 > a.total_query || len <= a.skip_len || len > a.query_len);
         L = live ? (int)len : 0;
       }
-      if (live && r * kBM < a.group * L) t = max(0, item_tiles(a, r, L, a.context_lens[b]));
+      if (live && r * BM < a.group * L) t = max(0, item_tiles<BM, BN>(a, r, L, a.context_lens[b]));
     }
     lds_n[o] = t;
     sum += max(t, 0);
@@ -391,14 +405,20 @@ __device__ SplitItem split_assign(const PrefillArgs& a, int* lds_n, int64_t* lds
   }
   __syncthreads();
   const int H = a.num_kv_heads;
-  const int64_t total = (lds_sum[0] + lds_sum[1] + lds_sum[2] + lds_sum[3]) * H;
-  const int hi = max(1, max(max(lds_red[0], lds_red[1]), max(lds_red[2], lds_red[3])));
+  int64_t total = 0;
+  int hi = 1;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    total += lds_sum[i];
+    hi = max(hi, lds_red[i]);
+  }
+  total *= H;
   // ceil(total / slots) in double precision (exact below 2^53, no 64-bit integer division)
   const int lo = (int)fmin((double)hi, fmax(2.0, ceil((double)total / (double)a.split_slots)));
-  const int step = max(1, (hi - lo + kThreads - 2) / (kThreads - 1));
+  const int step = max(1, (hi - lo + NT - 2) / (NT - 1));
   const int cap = a.kv_splits;
   {
-    const int cand = threadIdx.x == kThreads - 1 ? hi : min(hi, lo + (int)threadIdx.x * step);
+    const int cand = threadIdx.x == NT - 1 ? hi : min(hi, lo + (int)threadIdx.x * step);
     const float rc = 1.0f / (float)cand;
     const int capc = cap * cand;
     int count = 0;  // at most cap * pairs
@@ -415,7 +435,9 @@ __device__ SplitItem split_assign(const PrefillArgs& a, int* lds_n, int64_t* lds
     if (lane == 0) lds_red[w] = best;
   }
   __syncthreads();
-  const int T = min(min(lds_red[0], lds_red[1]), min(lds_red[2], lds_red[3]));
+  int T = lds_red[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) T = min(T, lds_red[i]);
   const float rT = 1.0f / (float)T;
   const int capT = cap * T;
   // wave 0: lane l takes a run of C pairs, a wave prefix sum gives each run's first part
@@ -449,16 +471,29 @@ __device__ SplitItem split_assign(const PrefillArgs& a, int* lds_n, int64_t* lds
   return found;
 }
 
-template <bool ALIGNED, int D, bool MASKED, bool GEN>
-__global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) pa_prefill_mfma(PrefillArgs a) {
-  using T = Tile<D>;
+// A work item is NW waves of 32 packed rows each, and K/V tiles hold BN keys:
+// NW = 4, BN = 64 (128 rows x 64 keys, the automatic prefill schedule), or
+// NW = 2, BN = 32 (64 rows x 32 keys: the tiling of the matrix kernel in
+// "Week 3 Day 5: Paged FlashAttention", Task 1, kept to measure against;
+// unmasked and never split).
+// (The second launch bound is read by the compiler as waves per SIMD for
+// these sizes: 2 keeps the register budget of two waves per SIMD in both.)
+template <bool ALIGNED, int D, bool MASKED, bool GEN, int NW, int BN>
+__global__ void __launch_bounds__(64 * NW, NW == 4 ? (MASKED ? 1 : Tile<D>::kBlocksPerCU) : (D <= 128 ? 2 : 1))
+    pa_prefill_mfma(PrefillArgs a) {
+  using T = Tile<D, BN>;
+  constexpr int kNT = 64 * NW;    // threads
+  constexpr int kRows = 32 * NW;  // packed rows of a work item
+  constexpr int kNB = BN / 32;    // 32-key score blocks per tile
+  constexpr int kSteps = BN / 16;  // 16-key P V steps per tile
+  static_assert((NW == 4 && BN == 64) || (NW == 2 && BN == 32 && !MASKED && !GEN), "work item geometries");
   __shared__ __attribute__((aligned(1024))) char lds_k0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char lds_k1[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v1[T::kBytes];
   __shared__ __attribute__((aligned(16))) int lds_n[kPrefillSplitTarget];  // split launches: tiles per pair
-  __shared__ int64_t lds_sum[kThreads / 64];
-  __shared__ int lds_red[kThreads / 64];
+  __shared__ int64_t lds_sum[kNT / 64];
+  __shared__ int lds_red[kNT / 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -476,7 +511,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   // split_assign.
   int item = (int)blockIdx.x, part = 0, n_parts = 1, u0 = 0;
   if (a.kv_splits > 1) {
-    const SplitItem si = split_assign(a, lds_n, lds_sum, lds_red);
+    const SplitItem si = split_assign<kNT, kRows, BN>(a, lds_n, lds_sum, lds_red);
     if (si.item < 0) return;  // past the list of parts (uniform across the workgroup)
     item = si.item;
     part = si.part;
@@ -499,13 +534,13 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
     start = s0;
   }
   const int R = G * L;  // packed rows of this sequence and kv head
-  const int q0 = rtile * kBM;
+  const int q0 = rtile * kRows;
   if (q0 >= R) return;  // a row tile past this sequence's rows (uniform across the work item)
   const int ctx = a.context_lens[b];
   const int offset = ctx - L;  // query position l sits at logical position l + offset
-  const int tile_last_pos = (min(q0 + kBM, R) - 1) / G;
+  const int tile_last_pos = (min(q0 + kRows, R) - 1) / G;
   const int kv_end = a.causal ? min(ctx, tile_last_pos + offset + 1) : ctx;
-  const int n_tiles_all = (kv_end + kBN - 1) / kBN;
+  const int n_tiles_all = (kv_end + BN - 1) / BN;
   // this workgroup's tiles [t_lo, n_tiles): part `part` of n_parts
   const int t_lo = (int)((int64_t)part * n_tiles_all / n_parts);
   const int n_tiles = (int)((int64_t)(part + 1) * n_tiles_all / n_parts);
@@ -527,11 +562,12 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
 
   // ---- first tile in flight before anything else ----
-  TilePages<ALIGNED, D> tp;
+  TilePages<ALIGNED, D, NW, BN> tp;
   if (n_tiles > t_lo) {
-    lookup_tile<ALIGNED, D, GEN>(a, bt_row, page_stride, head_off, ctx, t_lo * kBN, wave, lane, tp);
-    issue_tile<ALIGNED, D, GEN>(a, tp, ctx, t_lo * kBN, wave, lane, lds_k0, lds_v0);
-    lookup_tile<ALIGNED, D, GEN>(a, bt_row, page_stride, head_off, ctx, min(t_lo + 1, n_tiles - 1) * kBN, wave, lane, tp);
+    lookup_tile<ALIGNED, D, GEN, NW, BN>(a, bt_row, page_stride, head_off, ctx, t_lo * BN, wave, lane, tp);
+    issue_tile<ALIGNED, D, GEN, NW, BN>(a, tp, ctx, t_lo * BN, wave, lane, lds_k0, lds_v0);
+    lookup_tile<ALIGNED, D, GEN, NW, BN>(a, bt_row, page_stride, head_off, ctx, min(t_lo + 1, n_tiles - 1) * BN, wave,
+                                         lane, tp);
   }
 
   // ---- Q^T operand: lane holds row r0 + col, dims 16ks + 8half .. +8 ----
@@ -580,18 +616,18 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
   // statically (the loop is unrolled by two), so no wait is needed between
   // the next tile's loads and this tile's reads.
   auto tile_step = [&](int t, const char* kb_base, const char* vb_base, char* knext, char* vnext) {
-    const int t0 = t * kBN;
+    const int t0 = t * BN;
     wait_all_loads();  // this wave's part of tile t (and the next lookup) has landed
     __syncthreads();   // every wave's part is in LDS; every wave is done with tile t - 1
     const bool active = wave_has_rows && t0 < wave_kv_end;
     // mask entries of this lane's row for the tile's keys; issued before the
     // next tile's loads so that waiting for them does not wait for those
-    float mvals[MASKED ? 2 : 1][16];
+    float mvals[MASKED ? kNB : 1][16];
     if constexpr (MASKED) {
       if (active) {
         // elements 4j .. 4j+3 of a block are four consecutive keys (a multiple of 4 first)
   #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < kNB; ++kb)
   #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int k0 = t0 + 32 * kb + 8 * j + 4 * half;
@@ -608,23 +644,23 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
           }
       }
     }
-    if (t + 1 < n_tiles) issue_tile<ALIGNED, D, GEN>(a, tp, ctx, t0 + kBN, wave, lane, knext, vnext);
+    if (t + 1 < n_tiles) issue_tile<ALIGNED, D, GEN, NW, BN>(a, tp, ctx, t0 + BN, wave, lane, knext, vnext);
     // Lookup for tile t + 2 (clamped so that it is unconditional), done
     // after this tile's matrix work, not between the barrier and it.
-    const int t_look = min(t + 2, n_tiles - 1) * kBN;
+    const int t_look = min(t + 2, n_tiles - 1) * BN;
     if (!active) {
-      lookup_tile<ALIGNED, D, GEN>(a, bt_row, page_stride, head_off, ctx, t_look, wave, lane, tp);
+      lookup_tile<ALIGNED, D, GEN, NW, BN>(a, bt_row, page_stride, head_off, ctx, t_look, wave, lane, tp);
       return;
     }
 
-      // ---- S^T = K Q^T : two 32-key blocks ----
+      // ---- S^T = K Q^T : kNB 32-key blocks (two at 64-key tiles) ----
       // Contraction step ks runs the MFMAs of both blocks; the K fragments of
       // step ks + 2 are read from LDS meanwhile. The reads and their waits
       // are explicit: LDS reads complete in order, so before step ks only
       // the reads of the two later steps may still be in flight.
-      f32x16_t acc_s[2];
+      f32x16_t acc_s[kNB];
   #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kNB; ++kb)
   #pragma unroll
         for (int i = 0; i < 16; ++i) acc_s[kb][i] = 0.f;
       {
@@ -636,17 +672,18 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
         auto read_k = [&](int ks, u32x4_t (&dst)[2]) {
           const uint32_t a0 = kaddr0 ^ (uint32_t)(ks << 5);
           lds_read_b128<0>(dst[0], a0);
-          lds_read_b128<32 * 2 * D>(dst[1], a0);
+          if constexpr (kNB > 1) lds_read_b128<32 * 2 * D>(dst[1], a0);
         };
         read_k(0, kf[0]);
         read_k(1, kf[1]);
   #pragma unroll
         for (int ks = 0; ks < T::kKs; ++ks) {
           if (ks + 2 < T::kKs) read_k(ks + 2, kf[(ks + 2) % 3]);
-          const int younger = 2 * min(2, T::kKs - 1 - ks);  // reads issued after step ks's
-          lds_wait(younger, kf[ks % 3]);
+          const int younger = kNB * min(2, T::kKs - 1 - ks);  // reads issued after step ks's
+          if constexpr (kNB > 1) lds_wait(younger, kf[ks % 3]);
+          else lds_wait_n(younger, kf[ks % 3][0]);
   #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < kNB; ++kb)
             acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[ks % 3][kb]), qv[ks],
                                                                 acc_s[kb], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
@@ -654,7 +691,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
       }
 
       // V^T fragments of the first kVA P V groups: read during the softmax
-      constexpr int kVG = 4 * T::kDb;  // P V groups: (16-key step, 32-dim block)
+      constexpr int kVG = kSteps * T::kDb;  // P V groups: (16-key step, 32-dim block)
       constexpr int kVA = 3;           // groups read ahead
       const uint32_t vaddr0 = lds_addr(vb_base) + v_lane0, vaddr1 = lds_addr(vb_base) + v_lane1;
       u32x4_t vf[kVA + 1];
@@ -674,7 +711,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
       float cs = a.c;
       if constexpr (MASKED) {
   #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < kNB; ++kb)
   #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = t0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
@@ -682,10 +719,10 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
           }
         cs = 1.f;
       }
-      const bool need_mask = (t0 + kBN > ctx) || (a.causal && t0 + kBN - 1 > wave_first_pos + offset);
+      const bool need_mask = (t0 + BN > ctx) || (a.causal && t0 + BN - 1 > wave_first_pos + offset);
       if (need_mask) {
   #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < kNB; ++kb) {
   #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = t0 + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
@@ -694,9 +731,9 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
           }
         }
       }
-      float mx[2];
+      float mx[kNB];
   #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kNB; ++kb) {
         const float m0 = fmaxf(fmaxf(acc_s[kb][0], acc_s[kb][1]), acc_s[kb][2]);
         const float m1 = fmaxf(fmaxf(acc_s[kb][3], acc_s[kb][4]), acc_s[kb][5]);
         const float m2 = fmaxf(fmaxf(acc_s[kb][6], acc_s[kb][7]), acc_s[kb][8]);
@@ -704,7 +741,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
         const float m4 = fmaxf(fmaxf(acc_s[kb][12], acc_s[kb][13]), acc_s[kb][14]);
         mx[kb] = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), acc_s[kb][15]));
       }
-      const float tmax = max_xor32(fmaxf(mx[0], mx[1])) * cs;  // log2 units
+      const float tmax = max_xor32(fmaxf(mx[0], mx[kNB - 1])) * cs;  // log2 units
       // The exponent reference moves only when the tile maximum exceeds it by
       // more than kTau; otherwise the weights stay <= 2^kTau and the output
       // needs no rescale. The branch is taken when any row of the wave moves.
@@ -719,10 +756,10 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
           for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
       }
       const float neg_ref = m_run == -INFINITY ? 0.f : -m_run;
-      uint32_t pk[2][8];  // P^T operand, packed bf16 pairs
+      uint32_t pk[kNB][8];  // P^T operand, packed bf16 pairs
       float psum = 0.f;
   #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kNB; ++kb) {
   #pragma unroll
         for (int i = 0; i < 16; i += 2) {
           const float p0 = fast_exp2(fmaf(acc_s[kb][i], cs, neg_ref));
@@ -746,7 +783,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[g % (kVA + 1)]),
                                                             __builtin_bit_cast(bf16x8_t, pw), acc_o[db], 0, 0, 0);
       }
-      lookup_tile<ALIGNED, D, GEN>(a, bt_row, page_stride, head_off, ctx, t_look, wave, lane, tp);
+      lookup_tile<ALIGNED, D, GEN, NW, BN>(a, bt_row, page_stride, head_off, ctx, t_look, wave, lane, tp);
   };
   for (int t = t_lo; t < n_tiles; t += 2) {
     tile_step(t, lds_k0, lds_v0, lds_k1, lds_v1);
@@ -773,8 +810,8 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
     const size_t entry = (size_t)(u0 + part) * H + kvh;
     if (wave_has_rows) {
       const float l_tot = sum_xor32(l_run);
-      if (half == 0 && row_abs < R) store_coherent_x2(a.ws_ml + (entry * kBM + 32 * wave + col) * 2, f32x2_t{m_run, l_tot});
-      float* wp = a.ws_acc + (entry * 4 + wave) * kChunks * 256 + 4 * lane;
+      if (half == 0 && row_abs < R) store_coherent_x2(a.ws_ml + (entry * kRows + 32 * wave + col) * 2, f32x2_t{m_run, l_tot});
+      float* wp = a.ws_acc + (entry * NW + wave) * kChunks * 256 + 4 * lane;
 #pragma unroll
       for (int db = 0; db < T::kDb; ++db)
 #pragma unroll
@@ -793,7 +830,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
 #pragma unroll
     for (int s = 0; s < kPrefillMaxSplits; ++s) {
       const size_t e = (size_t)(u0 + min(s, n_parts - 1)) * H + kvh;
-      ml[s] = load_coherent_x2(a.ws_ml + (e * kBM + 32 * wave + col) * 2);
+      ml[s] = load_coherent_x2(a.ws_ml + (e * kRows + 32 * wave + col) * 2);
     }
     float M = -INFINITY;
 #pragma unroll
@@ -809,7 +846,7 @@ __global__ void __launch_bounds__(kThreads, MASKED ? 1 : Tile<D>::kBlocksPerCU) 
       f32x4_t av[kChunks];
       if (s != part) {
         const size_t e = (size_t)(u0 + s) * H + kvh;
-        const float* rp = a.ws_acc + (e * 4 + wave) * kChunks * 256 + 4 * lane;
+        const float* rp = a.ws_acc + (e * NW + wave) * kChunks * 256 + 4 * lane;
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) av[c] = load_coherent_x4(rp + c * 256);
       } else {
@@ -871,7 +908,7 @@ struct Residency {
   int cus, slots;
 };
 
-template <bool ALIGNED, int D, bool MASKED, bool GEN>
+template <bool ALIGNED, int D, bool MASKED, bool GEN, int NW, int BN>
 Residency resident_slots() {
   static Residency cache[64] = {};
   int dev = 0;
@@ -879,24 +916,29 @@ Residency resident_slots() {
   if (cache[dev].slots > 0) return cache[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)pa_prefill_mfma<ALIGNED, D, MASKED, GEN>, kThreads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)pa_prefill_mfma<ALIGNED, D, MASKED, GEN, NW, BN>, 64 * NW,
                                                    0) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   cache[dev] = Residency{cus, cus * per_cu};
   return cache[dev];
 }
 
-template <bool ALIGNED, int D, bool MASKED, bool GEN>
+template <bool ALIGNED, int D, bool MASKED, bool GEN, int NW = 4, int BN = kBN>
 hipError_t launch_instance(PrefillArgs a, const Plan& p, hipStream_t stream) {
   // split: one workgroup per workspace entry, the resident ones used
   const unsigned grid = (unsigned)(a.kv_splits > 1 ? kPrefillSplitTarget : p.num_work);
-  if (a.kv_splits > 1) a.split_slots = min(kPrefillSplitTarget, resident_slots<ALIGNED, D, MASKED, GEN>().slots);
-  hipLaunchKernelGGL((pa_prefill_mfma<ALIGNED, D, MASKED, GEN>), dim3(grid), dim3(kThreads), 0, stream, a);
+  if (a.kv_splits > 1) a.split_slots = min(kPrefillSplitTarget, resident_slots<ALIGNED, D, MASKED, GEN, NW, BN>().slots);
+  hipLaunchKernelGGL((pa_prefill_mfma<ALIGNED, D, MASKED, GEN, NW, BN>), dim3(grid), dim3(64 * NW), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D, bool MASKED>
 hipError_t launch_mask(const PrefillArgs& a, const Plan& p, hipStream_t stream) {
+  if constexpr (!MASKED) {
+    if (p.schedule == kSchedulePrefill64x32)  // native head dims only, never split (the plan's checks)
+      return p.aligned ? launch_instance<true, D, false, false, 2, 32>(a, p, stream)
+                       : launch_instance<false, D, false, false, 2, 32>(a, p, stream);
+  }
   if (a.dv != D)  // a head dim without an instance of its own: the next larger one, masked dims, per-row loader
     return launch_instance<false, D, MASKED, true>(a, p, stream);
   if (p.aligned) return launch_instance<true, D, MASKED, false>(a, p, stream);

@@ -76,6 +76,8 @@ int run_uniform(const void* query, const void* key_pages, const void* value_page
                                  page_size, max_pages, causal != 0);
   const int rc = pa::make_plan(s, schedule, decode_work_items, true, &plan, &err);
   if (rc != pa::kOk) return set_error(rc, err);
+  if (mask && plan.schedule == pa::kSchedulePrefill64x32)
+    return set_error(PA_ERR_UNSUPPORTED, "the 64 x 32 prefill tiling takes no explicit mask");
   if (plan.schedule == pa::kSchedulePrefill && plan.kv_splits > 1 &&
       (workspace == nullptr || workspace_bytes < plan.workspace_bytes)) {
     // a prefill without the workspace its key-range split needs runs unsplit

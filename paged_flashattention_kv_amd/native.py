@@ -27,6 +27,7 @@ PA_ERR_METADATA = -5
 SCHEDULE_AUTO = 0
 SCHEDULE_DECODE = 1
 SCHEDULE_PREFILL = 2
+SCHEDULE_PREFILL_64X32 = 3  # 64 query rows x 32 keys per tile; explicit only
 
 # Every symbol include/paged_attention.h declares.
 EXPORTED = (

@@ -54,7 +54,24 @@ int main() {
   }
   CHECK(pa::make_plan(shape(1, 32, 8, 100, 128, 16, 4), 0, 0, true, &p, &err) == pa::kErrInvalid);
   CHECK(pa::make_plan(shape(1, 32, 8, 100, 128, 16, 4, false), 0, 0, true, &p, &err) == pa::kOk);
-  CHECK(pa::make_plan(shape(1, 32, 8, 1, 128, 16, 4), 3, 0, true, &p, &err) == pa::kErrInvalid);
+  CHECK(pa::make_plan(shape(1, 32, 8, 1, 128, 16, 4), 4, 0, true, &p, &err) == pa::kErrInvalid);
+  CHECK(pa::make_plan(shape(1, 32, 8, 1, 128, 16, 4), -1, 0, true, &p, &err) == pa::kErrInvalid);
+  // the 64 x 32 prefill tiling: explicit, native head dims, 64-row tiles, never split
+  for (int D : {64, 128, 256}) {
+    CHECK(pa::make_plan(shape(4, 32, 8, 2048, D, 128, 16), 3, 0, true, &p, &err) == pa::kOk);
+    CHECK(p.schedule == pa::kSchedulePrefill64x32 && p.aligned && p.n_qtiles == 128 && p.num_work == 4096);
+    CHECK(p.kv_splits == 1 && p.workspace_bytes == 0);
+  }
+  CHECK(pa::make_plan(shape(8, 32, 8, 65, 128, 128, 30), 3, 0, true, &p, &err) == pa::kOk);
+  CHECK(p.n_qtiles == 5 && p.num_work == 320 && p.kv_splits == 1 && p.workspace_bytes == 0);
+  CHECK(pa::make_plan(shape(1, 4, 2, 13, 128, 32, 4), 3, 0, true, &p, &err) == pa::kOk);
+  CHECK(p.aligned && p.n_qtiles == 1);
+  CHECK(pa::make_plan(shape(1, 4, 2, 13, 128, 16, 4), 3, 0, true, &p, &err) == pa::kOk);
+  CHECK(!p.aligned);
+  CHECK(pa::make_plan(shape(1, 4, 2, 1, 128, 16, 4), 3, 0, true, &p, &err) == pa::kOk);
+  CHECK(p.schedule == pa::kSchedulePrefill64x32);  // explicit: even a one-row query
+  for (int D : {8, 80, 96, 192})
+    CHECK(pa::make_plan(shape(4, 32, 8, 64, D, 128, 16), 3, 0, true, &p, &err) == pa::kErrUnsupported);
   CHECK(pa::make_plan(shape(1, 32, 8, 1, 128, 16, 4), 1, -1, true, &p, &err) == pa::kErrInvalid);
   CHECK(pa::make_plan(shape(1, 32, 8, 1, 128, 16, 4), 1, 65537, true, &p, &err) == pa::kErrInvalid);
   CHECK(pa::make_plan(shape(1, 32, 8, 3, 128, 16, 4), 1, 0, true, &p, &err) == pa::kErrInvalid);

@@ -210,6 +210,12 @@ def test_schedule_rule_and_workspace(lib):
     assert native.schedule_for(1, 8, 8, 8, 128, 128, 33) == native.SCHEDULE_PREFILL
     assert native.schedule_for(4, 32, 8, 2048, 128, 128, 16) == native.SCHEDULE_PREFILL
     assert native.workspace_bytes(4, 32, 8, 2048, 128, 128, 16) == 0
+    # the 64 x 32 prefill tiling: no workspace (never split), native head dims only
+    assert native.workspace_bytes(8, 32, 8, 65, 128, 128, 30, native.SCHEDULE_PREFILL_64X32, 0) == 0
+    with pytest.raises(native.PagedAttentionError):
+        native.workspace_bytes(8, 32, 8, 65, 80, 128, 30, native.SCHEDULE_PREFILL_64X32, 0)
+    with pytest.raises(native.PagedAttentionError):
+        native.workspace_bytes(8, 32, 8, 65, 128, 128, 30, 4, 0)
     # decode: arrival counters plus two partial (max, sum, acc[D]) slots per work item and row
     n = native.workspace_bytes(16, 32, 8, 1, 128, 16, 2048)
     assert n >= 16 * 8 * 8 + 2048 * 2 * 4 * 130 * 4
