@@ -418,11 +418,18 @@ def mixed_roofline_us(p) -> dict:
     return {"decode_kv_bytes": dec_bytes, "prefill_flops": pre_flops, "bound_us": round(t * 1e6, 3)}
 
 
+def _traffic(spec, kernel, workload):
+    """``traffic``: True = the profile of (kernel, workload); a (kernel, workload) pair = that profile."""
+    if spec is True:
+        return measured_traffic(kernel, workload)
+    return measured_traffic(*spec) if spec else None
+
+
 def _hbm_roofline(byt, ms, kernel, workload, traffic=True, **more):
     g = byt / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(g, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(g / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(kernel, workload) if traffic else None,
+            "traffic": _traffic(traffic, kernel, workload),
             "kernel": kernel, "algorithmic_bytes_per_launch": byt, **more}
 
 
@@ -430,7 +437,7 @@ def _mfma_roofline(flops, ms, kernel, workload, traffic=True):
     tf = flops / (ms * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(kernel, workload) if traffic else None,
+            "traffic": _traffic(traffic, kernel, workload),
             "kernel": kernel, "algorithmic_flops_per_launch": flops}
 
 
@@ -448,7 +455,8 @@ def describe_extra(name: str, p, st: dict, info: dict) -> dict:
         return {"workload": "long_prefill at the stated tiling: 64 packed query rows x 32 keys per tile "
                             "(PA_SCHEDULE_PREFILL_64X32; the row above is the automatic 128 x 64 tiling)",
                 **timing, "value": round(tf, 2), "unit": "TFLOP/s",
-                "roofline": _mfma_roofline(p.flops(), ms, "pa_prefill_mfma (64x32)", "", traffic=False)}
+                "roofline": _mfma_roofline(p.flops(), ms, "pa_prefill_mfma (64x32)", "",
+                                           traffic=("pa_prefill_mfma", "long_prefill_64x32"))}
     if name == "chunked_continuation":
         return {"workload": "B=8 L=65 history U[1000,3600] (seed 4) H_q=32 H_kv=8 D=128 causal, page_size=128",
                 **timing, "tflops": round(p.flops() / (ms * 1e-3) / 1e12, 2),
@@ -471,13 +479,14 @@ def describe_extra(name: str, p, st: dict, info: dict) -> dict:
         byt = p.kv_bytes() + info["mask_bytes"]
         return {"workload": "decode_batch with an explicit fp32 mask [64, 32, 1, 4096] (N(0,1) log-weights, 10% -inf)",
                 **timing, "value": round(byt / (ms * 1e-3) / 1e12, 4), "unit": "TB/s",
-                "roofline": _hbm_roofline(byt, ms, "pa_decode_work (masked)", "", traffic=False,
-                                          mask_bytes=info["mask_bytes"])}
+                "roofline": _hbm_roofline(byt, ms, "pa_decode_work (masked)", "",
+                                          traffic=("pa_decode_work", "masked_decode"), mask_bytes=info["mask_bytes"])}
     if name == "masked_prefill":
         tf = p.flops() / (ms * 1e-3) / 1e12
         return {"workload": "long_prefill with an explicit fp32 mask [4, 1, 2048, 2048] shared by the heads",
                 **timing, "value": round(tf, 2), "unit": "TFLOP/s",
-                "roofline": _mfma_roofline(p.flops(), ms, "pa_prefill_mfma (masked)", "", traffic=False)}
+                "roofline": _mfma_roofline(p.flops(), ms, "pa_prefill_mfma (masked)", "",
+                                           traffic=("pa_prefill_mfma", "masked_prefill"))}
     if name == "mixed_batch":
         rl = mixed_roofline_us(p)
         return {"workload": f"mixed_batch: B={p.batch}, {int((p.query_lens > 1).sum())} prefill chunks (<=128 "
