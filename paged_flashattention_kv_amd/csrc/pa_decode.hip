@@ -64,7 +64,8 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 // Keys each lane holds per step (a wave step covers 8 * kTK keys), and the
 // number of register stages per wave: the K/V loads of the next
-// kStages - 1 steps are issued before the current step is computed.
+// kStages - 1 steps are issued before the current step is computed (one
+// stage fewer in the 4-row instances, see decode_piece).
 #ifndef PA_DECODE_TK
 #define PA_DECODE_TK 2
 #endif
@@ -562,22 +563,28 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int32_t* lds_b
     // keeps the number of outstanding loads the same on every path, so the
     // waits before each step cover only that step's own loads.
     constexpr int kStride = kWaves * kStep;
+    // register stages: the 4-row instances hold one fewer, which keeps the
+    // masked one within the two-wave register budget (two work items per CU)
+    // and measured faster for both (decode batch 107.6 -> 106.0 us, long
+    // decode 342 -> 336 us, masked decode batch 127 -> 109 us); with 1 and 2
+    // rows three stages measured 1-3% faster
+    constexpr int kSt = ROWS == 4 ? kStages - 1 : kStages;
     int t = ka + wave * kStep;
     if (t < kb) {
-      Stage st[kStages];
-      float mv[kStages][MASKED ? ROWS : 1][kTK];  // mask entries riding with each stage
+      Stage st[kSt];
+      float mv[kSt][MASKED ? ROWS : 1][kTK];  // mask entries riding with each stage
 #pragma unroll
-      for (int i = 0; i < kStages - 1; ++i) {
+      for (int i = 0; i < kSt - 1; ++i) {
         load_stage<ALIGNED, D, GEN>(g, t + i * kStride, st[i]);
         if constexpr (MASKED) load_mask<ROWS, D>(mrow, a.mask_len, t + i * kStride, kg, mv[i]);
       }
       bool done = false;
       while (!done) {
 #pragma unroll
-        for (int j = 0; j < kStages; ++j) {
-          load_stage<ALIGNED, D, GEN>(g, t + (kStages - 1) * kStride, st[(j + kStages - 1) % kStages]);
+        for (int j = 0; j < kSt; ++j) {
+          load_stage<ALIGNED, D, GEN>(g, t + (kSt - 1) * kStride, st[(j + kSt - 1) % kSt]);
           if constexpr (MASKED)
-            load_mask<ROWS, D>(mrow, a.mask_len, t + (kStages - 1) * kStride, kg, mv[(j + kStages - 1) % kStages]);
+            load_mask<ROWS, D>(mrow, a.mask_len, t + (kSt - 1) * kStride, kg, mv[(j + kSt - 1) % kSt]);
           compute_stage<ROWS, D, MASKED>(st[j], mv[j], t, kb, a.mask_len, q, last, min_last, a.c, kg, rs);
           t += kStride;
           if (t >= kb) {
@@ -723,9 +730,9 @@ __device__ void merge_segment(const DecodeArgs& a, int32_t* lds_parts, int b, in
 }
 
 // Two resident workgroups per CU (a register budget of 256 per lane) for the
-// instances that fit it; the 8-row and masked ones take one.
+// instances that fit it; the 8-row ones take one.
 template <int ROWS, bool ALIGNED, int D, bool MASKED, bool GEN>
-__global__ void __launch_bounds__(kThreads, (ROWS <= 4 && !MASKED) ? 2 : 1) pa_decode_work(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, ROWS <= 4 ? 2 : 1) pa_decode_work(DecodeArgs a) {
   extern __shared__ int32_t lds_bt[];
   __shared__ float lds_m[kWaves][ROWS];
   __shared__ float lds_l[kWaves][ROWS];
