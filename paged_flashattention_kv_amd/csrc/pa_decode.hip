@@ -91,7 +91,7 @@ constexpr float kTau = 8.0f;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
 constexpr int kGran = 64;    // keys per granule: work ranges start and end on granules
-// The work split's cost model (see WorkSplit): a segment start costs 4
+// The work split's cost model (see WorkSplit): a segment start costs 2
 // granules, and the grid's second half gets 12/16 of the first half's share.
 // Measured on the decode batch (per-workgroup timestamps): a piece costs 6-8
 // us of fixed latency (about 3 granules of streaming) and the second
@@ -99,8 +99,11 @@ constexpr int kGran = 64;    // keys per granule: work ranges start and end on g
 // items (five pieces, second half) ended 25-30 us after the median. A/B on one
 // MI355X: decode batch 115.6 -> 107.8 us; long-context decode 333.5 -> 341.2
 // us (its segments are long and uniform, so it gains nothing and pays the
-// skew).
-constexpr int kSplitPieceCost = 4;  // granules a segment start costs in the work split
+// skew). With two register stages in the 4-row instances a start cost of 2
+// granules replaced 4 (decode batch 105.8-106.2 -> 104.1-104.6 us, masked
+// decode and mixed batch ~1% faster, long decode 0.6% slower; 1 granule:
+// 111.9 us, 3: 105.4 us).
+constexpr int kSplitPieceCost = 2;  // granules a segment start costs in the work split
 constexpr int kSplitWa = 16;        // weight of the grid's first half
 constexpr int kSplitWb = 12;        // weight of the grid's second half
 constexpr int kWindow = 2048;  // keys per block-table staging window
