@@ -65,9 +65,11 @@ int make_plan(const Shape& s, int schedule, int decode_work_items, bool check_po
       return fail(err, kErrInvalid, "decode_work_items must be in [0, 65536]");
     p.work_items = decode_work_items;
     p.work_cap = decode_work_items > 0 ? decode_work_items : kDecodeAutoCap;
-    // granule arithmetic (work item * total granules) must stay inside int64
+    // the work split's products must stay inside int64: cost units (at most
+    // 3x the granules, a segment start costing 2) times the weight before a
+    // work item (at most 16 per item, times work_cap items), with room to spare
     const int64_t granules = s.batch * s.num_kv_heads * cdiv(max_ctx, 64);
-    if (granules > (int64_t(1) << 62) / p.work_cap)
+    if (granules > (int64_t(1) << 53) / p.work_cap)
       return fail(err, kErrUnsupported, "decode work too large for the granule arithmetic");
     p.bt_entries = int(kDecodeWindow / s.page_size + 2);
     p.aligned = s.page_size % decode_step(s.head_dim) == 0;  // a wave step lies inside one page

@@ -77,6 +77,9 @@ int main() {
   CHECK(pa::make_plan(shape(1, 32, 8, 3, 128, 16, 4), 1, 0, true, &p, &err) == pa::kErrInvalid);
   CHECK(pa::make_plan(shape(1, 32, 8, 1, 128, 1 << 20, 1 << 12), 0, 0, true, &p, &err) == pa::kErrUnsupported);
   CHECK(!err.empty());
+  // the decode work split's products: granules * work items at most 2^53 (2^43 granules here)
+  CHECK(pa::make_plan(shape(1 << 16, 8, 8, 1, 128, 1 << 14, 1 << 16), 1, 0, true, &p, &err) == pa::kErrUnsupported);
+  CHECK(pa::make_plan(shape(1 << 14, 8, 8, 1, 128, 1 << 14, 1 << 16), 1, 0, true, &p, &err) == pa::kOk);
   // dispatch on the query length
   for (int L = 1; L <= 64; ++L) {
     for (int G : {1, 2, 4, 8}) {
