@@ -100,10 +100,13 @@ constexpr int kGran = 64;    // keys per granule: work ranges start and end on g
 // MI355X: decode batch 115.6 -> 107.8 us; long-context decode 333.5 -> 341.2
 // us (its segments are long and uniform, so it gains nothing and pays the
 // skew). With two register stages in the 4-row instances a start cost of 2
-// granules replaced 4 (decode batch 105.8-106.2 -> 104.1-104.6 us, masked
-// decode and mixed batch ~1% faster, long decode 0.6% slower; 1 granule:
-// 111.9 us, 3: 105.4 us).
-constexpr int kSplitPieceCost = 2;  // granules a segment start costs in the work split
+// granules replaced 4 where two work items share a CU (decode batch
+// 105.8-106.2 -> 104.1-104.6 us, masked decode and mixed batch ~1% faster,
+// long decode 0.6% slower, 1 and 2 rows unchanged; 1 granule: 111.9 us, 3:
+// 105.4 us); the 8-row instance, one work item per CU, keeps 4 (2 measured
+// 6% slower there).
+template <int ROWS>
+constexpr int split_piece_cost() { return ROWS <= 4 ? 2 : 4; }  // granules a segment start costs
 constexpr int kSplitWa = 16;        // weight of the grid's first half
 constexpr int kSplitWb = 12;        // weight of the grid's second half
 constexpr int kWindow = 2048;  // keys per block-table staging window
@@ -440,12 +443,13 @@ __device__ __forceinline__ int64_t granule_of(const WorkSplit& s, int64_t x, int
 // The split for this launch: the cost terms only when every work item still
 // gets at least one granule (each range longer than a segment start's cost),
 // else the even split of granules.
+template <int ROWS>
 __device__ __forceinline__ WorkSplit make_split(const DecodeArgs& a, int64_t gran_per_head, int64_t nonempty) {
   WorkSplit s;
   s.T = gran_per_head * a.num_kv_heads;
   s.P = a.work_items;
   s.H = s.P / 2;
-  s.c = kSplitPieceCost;
+  s.c = split_piece_cost<ROWS>();
   s.C = s.T + (int64_t)s.c * nonempty * a.num_kv_heads;
   s.Wt = kSplitWa * s.H + kSplitWb * (s.P - s.H);
   const bool ok = s.T >= s.P && s.P >= 2 && s.C * min(kSplitWa, kSplitWb) >= (int64_t)(s.c + 2) * s.Wt;
@@ -768,7 +772,7 @@ __global__ void __launch_bounds__(kThreads, ROWS <= 4 ? 2 : 1) pa_decode_work(De
   }
   // every lane computes the same split: scalar registers
   const int64_t all = uniform64(lds_scan[kThreads - 1]);
-  const WorkSplit sp = make_split(a, all & kGMask, all >> kZShift);
+  const WorkSplit sp = make_split<ROWS>(a, all & kGMask, all >> kZShift);
   const int64_t hk = a.num_kv_heads;
   const int64_t w = blockIdx.x;
   const int64_t x0 = cost_begin(sp, w), x1 = cost_begin(sp, w + 1);
