@@ -25,7 +25,7 @@ constexpr int kDecodeMaxRows = 8;    // q rows (GQA group x query_len) per decod
 // per kv head stay within kDecodeAutoRows. Measured over query lengths 1-16,
 // contexts 128-32768 and GQA 1, 4 and 8 (16 sequences, Qwen3-4B head
 // count): with 6 or 8 rows the tiled prefill schedule was faster at every
-// context (1.4-1.9x); with up to 4 rows the decode schedule wins once a call
+// context (1.2-2.8x); with up to 4 rows the decode schedule wins once a call
 // streams several hundred MB of K/V, and it balances ragged batches.
 constexpr int kDecodeAutoRows = 4;
 constexpr int kDecodeWindow = 2048;  // keys whose block-table entries a decode work item stages at once
