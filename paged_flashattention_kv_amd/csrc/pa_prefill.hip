@@ -65,9 +65,7 @@ namespace pa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBM = kPrefillBlockM;       // 128 query rows
-constexpr int kBN = kPrefillBlockN;       // 64 keys
+constexpr int kBN = kPrefillBlockN;  // 64 keys per K/V tile (the automatic geometry)
 
 // Geometry for head dim D (64, 128 or 256): a key row is 2D bytes = D/8
 // chunks of 16 bytes; one global_load_lds instruction (64 lanes x 16 bytes)
