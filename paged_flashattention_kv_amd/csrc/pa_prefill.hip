@@ -215,22 +215,59 @@ __device__ __forceinline__ void lookup_tile(const PrefillArgs& a, const int32_t*
 // one page: a wave-uniform base (scalar registers) plus a per-lane byte
 // offset that is the same for every tile, so its loads cost no vector
 // arithmetic.
+// Word 3 of a raw (untyped, stride 0) buffer resource on gfx950: 32-bit data
+// format, every other field zero.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// 16 bytes per lane from base + off into LDS at dst + 16 * lane, through a
+// raw buffer over [base, base + bytes): base and size sit in scalar registers
+// (the resource is built there), the lane's 32-bit offset is the only vector
+// operand, so the load costs no vector instruction, and an offset past the
+// buffer reads zeros instead of leaving it. The host compilation pass has no
+// buffer-resource type and never runs this code.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, int bytes, uint32_t off, char* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRawBufferWord3), (lds_void*)dst,
+      16, off, 0, 0, 0);
+#endif
+}
+
+// The per-lane byte offsets of a whole aligned tile's loads from its first
+// row, computed once per work item (the empty asm statement keeps the
+// compiler from re-deriving them inside the tile loop).
+template <int D, int NW, int BN>
+struct TileOffsets {
+  uint32_t off[Stage<D, NW, BN>::kInsts];
+};
+
+template <int D, bool GEN, int NW, int BN>
+__device__ __forceinline__ void tile_offsets(const PrefillArgs& a, int wave, int lane, TileOffsets<D, NW, BN>& to) {
+  using T = Tile<D>;
+  using S = Stage<D, NW, BN>;
+#pragma unroll
+  for (int i = 0; i < S::kInsts; ++i) {
+    const int key = S::kKeys * wave + T::kRowsPerInst * i + lane / T::kChunks;  // key inside the tile
+    const int chunk = src_chunk<GEN>(a, (lane % T::kChunks) ^ swz<D>(key));
+    uint32_t off = (uint32_t)(key * (GEN ? a.dv : D) + chunk * 8) * 2u;  // bytes from the tile's first row
+    asm volatile("" : "+v"(off));
+    to.off[i] = off;
+  }
+}
+
 template <bool ALIGNED, int D, bool GEN, int NW, int BN>
-__device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages<ALIGNED, D, NW, BN>& tp, int ctx,
-                                           int t0, int wave, int lane, char* kbuf, char* vbuf) {
+__device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages<ALIGNED, D, NW, BN>& tp,
+                                           const TileOffsets<D, NW, BN>& to, int ctx, int t0, int wave, int lane,
+                                           char* kbuf, char* vbuf) {
   using T = Tile<D>;
   using S = Stage<D, NW, BN>;
   if (ALIGNED && t0 + BN <= ctx) {
-    const char* kbase = reinterpret_cast<const char*>(a.kpages + tp.row[0]);
-    const char* vbase = reinterpret_cast<const char*>(a.vpages + tp.row[0]);
+    const int span = BN * (GEN ? a.dv : D) * 2;  // bytes of the tile's rows
 #pragma unroll
     for (int i = 0; i < S::kInsts; ++i) {
-      const int key = S::kKeys * wave + T::kRowsPerInst * i + lane / T::kChunks;  // key inside the tile
-      const int chunk = src_chunk<GEN>(a, (lane % T::kChunks) ^ swz<D>(key));
-      const uint32_t off = (uint32_t)(key * (GEN ? a.dv : D) + chunk * 8) * 2u;  // bytes from the tile's first row
       const int lds_off = wave * S::kKeys * 2 * D + i * 1024;
-      __builtin_amdgcn_global_load_lds((global_void*)(kbase + off), (lds_void*)(kbuf + lds_off), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_void*)(vbase + off), (lds_void*)(vbuf + lds_off), 16, 0, 0);
+      buffer_load_lds16(a.kpages + tp.row[0], span, to.off[i], kbuf + lds_off);
+      buffer_load_lds16(a.vpages + tp.row[0], span, to.off[i], vbuf + lds_off);
     }
     return;
   }
@@ -563,10 +600,12 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? Tile<D>::kBlocksPerCU : (D 
   const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
 
   // ---- first tile in flight before anything else ----
+  TileOffsets<D, NW, BN> to;
+  if (ALIGNED) tile_offsets<D, GEN, NW, BN>(a, wave, lane, to);
   TilePages<ALIGNED, D, NW, BN> tp;
   if (n_tiles > t_lo) {
     lookup_tile<ALIGNED, D, GEN, NW, BN>(a, bt_row, page_stride, head_off, ctx, t_lo * BN, wave, lane, tp);
-    issue_tile<ALIGNED, D, GEN, NW, BN>(a, tp, ctx, t_lo * BN, wave, lane, lds_k0, lds_v0);
+    issue_tile<ALIGNED, D, GEN, NW, BN>(a, tp, to, ctx, t_lo * BN, wave, lane, lds_k0, lds_v0);
     lookup_tile<ALIGNED, D, GEN, NW, BN>(a, bt_row, page_stride, head_off, ctx, min(t_lo + 1, n_tiles - 1) * BN, wave,
                                          lane, tp);
   }
@@ -645,7 +684,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? Tile<D>::kBlocksPerCU : (D 
           }
       }
     }
-    if (t + 1 < n_tiles) issue_tile<ALIGNED, D, GEN, NW, BN>(a, tp, ctx, t0 + BN, wave, lane, knext, vnext);
+    if (t + 1 < n_tiles) issue_tile<ALIGNED, D, GEN, NW, BN>(a, tp, to, ctx, t0 + BN, wave, lane, knext, vnext);
     // Lookup for tile t + 2 (clamped so that it is unconditional), done
     // after this tile's matrix work, not between the barrier and it.
     const int t_look = min(t + 2, n_tiles - 1) * BN;
