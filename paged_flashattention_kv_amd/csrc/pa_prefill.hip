@@ -58,6 +58,8 @@
 // apart, on one XCD (shared L2) when that is a multiple of 8; split, all
 // parts of one kv head run on one XCD when there are 8 kv heads.
 
+#include <utility>
+
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -219,27 +221,41 @@ __device__ __forceinline__ void lookup_tile(const PrefillArgs& a, const int32_t*
 // format, every other field zero.
 constexpr int kRawBufferWord3 = 0x00020000;
 
-// 16 bytes per lane from base + off into LDS at dst + 16 * lane, through a
-// raw buffer over [base, base + bytes): base and size sit in scalar registers
-// (the resource is built there), the lane's 32-bit offset is the only vector
-// operand, so the load costs no vector instruction, and an offset past the
-// buffer reads zeros instead of leaving it. The host compilation pass has no
-// buffer-resource type and never runs this code.
+// 16 bytes per lane from base + off + IMM into LDS at dst + IMM + 16 * lane,
+// through a raw buffer over [base, base + bytes): base and size sit in scalar
+// registers (the resource is built there), the lane's 32-bit offset is the
+// only vector operand, so the load costs no vector instruction, and an offset
+// past the buffer reads zeros instead of leaving it. The instruction's
+// immediate offset IMM moves the source and the LDS destination alike (the
+// LDS address is M0 + IMM + 16 * lane), so loads whose destinations differ by
+// IMM share one M0 value. The host compilation pass has no buffer-resource
+// type and never runs this code.
+template <int IMM = 0>
 __device__ __forceinline__ void buffer_load_lds16(const void* base, int bytes, uint32_t off, char* dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRawBufferWord3), (lds_void*)dst,
-      16, off, 0, 0, 0);
+      16, off, 0, IMM, 0);
 #endif
 }
 
 // The per-lane byte offsets of a whole aligned tile's loads from its first
 // row, computed once per work item (the empty asm statement keeps the
-// compiler from re-deriving them inside the tile loop).
+// compiler from re-deriving them inside the tile loop). Load i fills LDS
+// bytes [1024 i, 1024 i + 1024) of the wave's part of the tile; when key rows
+// have the LDS row length (no head-dim padding), its source also starts
+// 1024 i bytes further into the page. The immediate offset field holds 12
+// bits, so loads go in groups of four: group i / 4 has its own M0 (4096
+// bytes apart) and load i carries 1024 * (i % 4) as its immediate, which the
+// stored offset leaves out (every lane's key of load i is at least
+// kRowsPerInst * i, so the difference stays non-negative).
 template <int D, int NW, int BN>
 struct TileOffsets {
   uint32_t off[Stage<D, NW, BN>::kInsts];
 };
+
+constexpr int kInstBytes = 1024;  // LDS bytes one load instruction fills (64 lanes x 16)
+constexpr int kImmGroup = 4;      // loads per M0 value: immediates 0 .. 3072 stay below 4096
 
 template <int D, bool GEN, int NW, int BN>
 __device__ __forceinline__ void tile_offsets(const PrefillArgs& a, int wave, int lane, TileOffsets<D, NW, BN>& to) {
@@ -250,9 +266,22 @@ __device__ __forceinline__ void tile_offsets(const PrefillArgs& a, int wave, int
     const int key = S::kKeys * wave + T::kRowsPerInst * i + lane / T::kChunks;  // key inside the tile
     const int chunk = src_chunk<GEN>(a, (lane % T::kChunks) ^ swz<D>(key));
     uint32_t off = (uint32_t)(key * (GEN ? a.dv : D) + chunk * 8) * 2u;  // bytes from the tile's first row
+    if (!GEN) off -= (uint32_t)(kInstBytes * (i % kImmGroup));
     asm volatile("" : "+v"(off));
     to.off[i] = off;
   }
+}
+
+// The loads of a whole aligned tile without head-dim padding: one M0 value
+// per group of four loads, load i placed by its immediate offset.
+template <int D, int NW, int BN, size_t... I>
+__device__ __forceinline__ void issue_tile_imm(const void* kbase, const void* vbase, int span,
+                                               const TileOffsets<D, NW, BN>& to, char* kdst, char* vdst,
+                                               std::index_sequence<I...>) {
+  (buffer_load_lds16<kInstBytes * ((int)I % kImmGroup)>(kbase, span, to.off[I],
+                                                         kdst + kInstBytes * kImmGroup * ((int)I / kImmGroup)), ...);
+  (buffer_load_lds16<kInstBytes * ((int)I % kImmGroup)>(vbase, span, to.off[I],
+                                                         vdst + kInstBytes * kImmGroup * ((int)I / kImmGroup)), ...);
 }
 
 template <bool ALIGNED, int D, bool GEN, int NW, int BN>
@@ -263,11 +292,17 @@ __device__ __forceinline__ void issue_tile(const PrefillArgs& a, const TilePages
   using S = Stage<D, NW, BN>;
   if (ALIGNED && t0 + BN <= ctx) {
     const int span = BN * (GEN ? a.dv : D) * 2;  // bytes of the tile's rows
+    const int wave_off = wave * S::kKeys * 2 * D;  // the wave's part of the LDS tile
+    if constexpr (!GEN) {
+      issue_tile_imm<D, NW, BN>(a.kpages + tp.row[0], a.vpages + tp.row[0], span, to, kbuf + wave_off,
+                                vbuf + wave_off, std::make_index_sequence<S::kInsts>{});
+    } else {
 #pragma unroll
-    for (int i = 0; i < S::kInsts; ++i) {
-      const int lds_off = wave * S::kKeys * 2 * D + i * 1024;
-      buffer_load_lds16(a.kpages + tp.row[0], span, to.off[i], kbuf + lds_off);
-      buffer_load_lds16(a.vpages + tp.row[0], span, to.off[i], vbuf + lds_off);
+      for (int i = 0; i < S::kInsts; ++i) {
+        const int lds_off = wave_off + i * kInstBytes;
+        buffer_load_lds16(a.kpages + tp.row[0], span, to.off[i], kbuf + lds_off);
+        buffer_load_lds16(a.vpages + tp.row[0], span, to.off[i], vbuf + lds_off);
+      }
     }
     return;
   }
