@@ -35,7 +35,8 @@
 //
 // Page-translating loader ("Week 3 Day 5", Task 1): each K/V tile is
 // resolved through block_table while it is staged, straight from HBM into
-// LDS (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l). A
+// LDS by LDS DMA (global_load_lds_dwordx4, or buffer_load_dwordx4 ... lds for
+// a whole aligned tile: lane l's 16 bytes land at base + 16 l). A
 // wave instruction moves 1 KiB: 4 key rows of 256 bytes at head dim 128 (8
 // rows at 64, 2 at 256). Rows are stored with their 16-byte chunks
 // XOR-swizzled by the key index so that both the K fragment reads and the V
