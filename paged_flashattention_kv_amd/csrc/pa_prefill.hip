@@ -257,6 +257,7 @@ struct TileOffsets {
 
 constexpr int kInstBytes = 1024;  // LDS bytes one load instruction fills (64 lanes x 16)
 constexpr int kImmGroup = 4;      // loads per M0 value: immediates 0 .. 3072 stay below 4096
+static_assert(kInstBytes * (kImmGroup - 1) < 4096, "buffer immediate offsets hold 12 bits");
 
 template <int D, bool GEN, int NW, int BN>
 __device__ __forceinline__ void tile_offsets(const PrefillArgs& a, int wave, int lane, TileOffsets<D, NW, BN>& to) {
